@@ -1,0 +1,306 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs fwd,bwd,decode]
+                    [--no-cpu-baseline] [--aux]
+
+One step runs the whole path once, each leg on its own synthetic workload with
+inputs already resident in HBM:
+
+  fwd     causal GQA forward, B1 Hq32 Hkv8 N16384 D128, bf16, LSE saved
+  bwd     causal recompute backward, B2 H16 N4096 D128, bf16 (D_i pre-pass, dK/dV
+          tile kernel with dQ atomics, dQ conversion); O and LSE come from fa_fwd
+          on the same inputs before timing
+  decode  split-KV decode, 64 sequences x 1 token, Hq32 Hkv8 D128, bf16 cache,
+          lengths U[1024, 32768] (seed 0), chunks of 2048 + merge
+
+Throughput counts only matmul FLOPs over the (query, key) pairs that exist:
+4*D per pair for the forward and the decode (QK^T and PV), 10*D per pair for the
+backward (five products, one of them the recompute of S).  Decode bandwidth counts
+each valid cached K/V byte once plus q and O.
+
+Prints one JSON line.  The CPU baseline times the fp64 oracle forward on a bounded
+sample (whole query heads of the forward workload) on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import io_aware_tiled_10_amd as fa  # noqa: E402
+from io_aware_tiled_10_amd import inputs  # noqa: E402
+
+METRIC = "attention fwd/bwd TFLOP/s & % bf16 MFMA peak; split-KV decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+DEV = "cuda:0"
+
+FWD_CFG = dict(B=1, Hq=32, Hkv=8, N=16384, D=128, causal=True)
+BWD_CFG = dict(B=2, H=16, N=4096, D=128, causal=True)
+DEC_CFG = dict(Bs=64, Hq=32, Hkv=8, D=128, lo=1024, hi=32768, split=2048, lmax=32768)
+AUX_CFGS = {"fwd_b4h16n2048_noncausal": dict(B=4, Hq=16, Hkv=16, N=2048, D=128, causal=False),
+            "fwd_b4h16n2048_causal": dict(B=4, Hq=16, Hkv=16, N=2048, D=128, causal=True)}
+
+FWD_KERNEL_SRC = os.path.join(ROOT, "io_aware_tiled_10_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_b1h32kv8n16384d128_causal_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pairs(nq: int, nk: int, causal: bool) -> int:
+    """Number of (query, key) pairs that exist; causal: j <= i + (nk - nq)."""
+    if not causal:
+        return nq * nk
+    return int(np.clip(np.arange(nq, dtype=np.int64) + (nk - nq) + 1, 0, nk).sum())
+
+
+def bf16_dev(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(x).to(DEV).to(torch.bfloat16)
+
+
+# ------------------------------------------------------------------------------------
+# workloads
+# ------------------------------------------------------------------------------------
+
+class FwdLeg:
+    def __init__(self, cfg, seed=0):
+        self.cfg = cfg
+        x = inputs.attention_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["N"], cfg["D"], "bf16", seed)
+        self.q, self.k, self.v = bf16_dev(x.q), bf16_dev(x.k), bf16_dev(x.v)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:3], dtype=torch.float32, device=DEV)
+        self.flops = 4 * cfg["D"] * pairs(cfg["N"], cfg["N"], cfg["causal"]) * cfg["B"] * cfg["Hq"]
+
+    def run(self):
+        fa.fwd(self.q, self.k, self.v, causal=self.cfg["causal"], out=self.o, lse_out=self.lse)
+
+
+class BwdLeg:
+    def __init__(self, cfg, seed=0):
+        self.cfg = cfg
+        B, H, N, D = cfg["B"], cfg["H"], cfg["N"], cfg["D"]
+        x = inputs.attention_inputs(B, H, H, N, N, D, "bf16", seed, with_grad=True)
+        self.q, self.k, self.v, self.do = bf16_dev(x.q), bf16_dev(x.k), bf16_dev(x.v), bf16_dev(x.do)
+        self.o, self.lse = fa.fwd(self.q, self.k, self.v, causal=cfg["causal"])
+        self.grads = (torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v))
+        need = fa.binding.bwd_workspace_bytes(self.q, self.k, self.v)
+        self.ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+        self.flops = 10 * D * pairs(N, N, cfg["causal"]) * B * H
+
+    def run(self):
+        fa.bwd(self.q, self.k, self.v, self.o, self.do, self.lse, causal=self.cfg["causal"],
+               workspace=self.ws, grads=self.grads)
+
+
+class DecodeLeg:
+    def __init__(self, cfg, seed=0):
+        self.cfg = cfg
+        d = inputs.decode_inputs(cfg["Bs"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["lo"], cfg["hi"], seed)
+        self.lens = d.seq_lens
+        shape = (cfg["Bs"], cfg["Hkv"], cfg["lmax"], cfg["D"])
+        self.kc = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+        self.vc = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+
+        def fill(s):
+            kb, vb = d.kv_bits(s)
+            return s, kb, vb
+
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+            for s, kb, vb in ex.map(fill, range(cfg["Bs"])):
+                L = int(self.lens[s])
+                self.kc[s, :, :L] = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(DEV)
+                self.vc[s, :, :L] = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(DEV)
+        self.q = bf16_dev(d.q)
+        self.sl = torch.tensor(self.lens, dtype=torch.int32, device=DEV)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device=DEV)
+        a = fa.binding.decode_args(self.q, self.kc, self.vc, self.sl, self.o, self.lse, cfg["lmax"],
+                                   cfg["split"], None)
+        import ctypes
+        self.ws = torch.empty(fa.lib().fa_decode_workspace_bytes(ctypes.byref(a)), dtype=torch.uint8,
+                              device=DEV)
+        tot = int(self.lens.sum())
+        D, Hq, Hkv = cfg["D"], cfg["Hq"], cfg["Hkv"]
+        self.flops = 4 * D * tot * Hq
+        self.bytes = 2 * Hkv * D * 2 * tot + cfg["Bs"] * Hq * D * 2 * 2 + cfg["Bs"] * Hq * 4
+
+    def run(self):
+        fa.decode(self.q, self.kc, self.vc, self.sl, max_len=self.cfg["lmax"], split_len=self.cfg["split"],
+                  workspace=self.ws, out=self.o, lse_out=self.lse)
+
+
+# ------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on whole query heads of the forward workload
+# ------------------------------------------------------------------------------------
+
+def cpu_baseline(budget_s: float = 12.0):
+    import oracle
+
+    cfg = FWD_CFG
+    x = inputs.attention_inputs(1, cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["N"], cfg["D"], "bf16", 0)
+    G = cfg["Hq"] // cfg["Hkv"]
+    per_head = 4 * cfg["D"] * pairs(cfg["N"], cfg["N"], cfg["causal"])
+    done, t0 = 0, time.perf_counter()
+    while done < cfg["Hq"]:
+        h = done
+        oracle.attn_fwd(x.q[:, h:h + 1], x.k[:, h // G:h // G + 1], x.v[:, h // G:h // G + 1], None, True)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    return {"value": round(per_head * done / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle forward on {done} whole query head(s) of the B1 Hq32 Hkv8 N16384 "
+                      f"D128 causal workload ({done * per_head / 1e9:.1f} GFLOP credited, {el:.1f} s)"}
+
+
+def traffic_for(kernel_src: str, path: str):
+    """HBM bytes per launch from the committed counter summary, if it is current."""
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_sha256") != h:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--legs", default="fwd,bwd,decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--aux", action="store_true", help="also time the B4 H16 N2048 forwards")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the forward shards over heads with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if not fa.device_supported(0):
+        print("cuda:0 is not gfx950", file=sys.stderr)
+        sys.exit(1)
+
+    legs_wanted = [s for s in args.legs.split(",") if s]
+    log("setting up inputs ...")
+    legs = {}
+    if "fwd" in legs_wanted:
+        legs["fwd"] = FwdLeg(FWD_CFG)
+    if "bwd" in legs_wanted:
+        legs["bwd"] = BwdLeg(BWD_CFG)
+    if "decode" in legs_wanted:
+        legs["decode"] = DecodeLeg(DEC_CFG)
+    torch.cuda.synchronize()
+    log("inputs resident; warmup")
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for leg in legs.values():
+            leg.run()
+    torch.cuda.synchronize()
+
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for n in legs}
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        for n, leg in legs.items():
+            ev[n][i][0].record(stream)
+            leg.run()
+            ev[n][i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    leg_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in legs}
+    log(f"timed {args.steps} steps: {total_ms:.2f} ms (host wall {wall * 1e3:.2f} ms)")
+
+    out_legs = {}
+    flops = 0
+    for n, leg in legs.items():
+        ms = leg_ms[n]
+        tf = leg.flops / (ms * 1e-3) / 1e12
+        flops += leg.flops
+        rec = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        if n == "decode":
+            gbs = leg.bytes / (ms * 1e-3) / 1e9
+            rec.update({"hbm_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                        "algorithmic_bytes": int(leg.bytes)})
+        out_legs[n] = rec
+
+    if args.aux:
+        for name, cfg in AUX_CFGS.items():
+            leg = FwdLeg(cfg)
+            for _ in range(3):
+                leg.run()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(20):
+                leg.run()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / 20
+            tf = leg.flops / (ms * 1e-3) / 1e12
+            out_legs[name] = {"ms": round(ms, 4), "tflops": round(tf, 2),
+                              "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "in_step": False}
+            del leg
+
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    roofline = None
+    if "fwd" in legs:
+        ach = legs["fwd"].flops / (leg_ms["fwd"] * 1e-3) / 1e12
+        roofline = {"kernel": "fwd_bf16_kernel<128> (one launch per fa_fwd call)", "bound": "mfma",
+                    "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic_for(FWD_KERNEL_SRC, TRAFFIC_FILE)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "one step = fwd B1 Hq32 Hkv8 N16384 D128 causal + bwd B2 H16 N4096 D128 "
+                               "causal + split-KV decode 64 seqs Hq32 Hkv8 D128 L~U[1024,32768] split 2048",
+                   "legs": list(legs), "seed": 0, "global_batch": None, "parallelism": "single GPU"},
+        "legs": out_legs,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

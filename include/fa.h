@@ -1,0 +1,207 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa.so).
+ *
+ * Three calls, one per part of the method:
+ *
+ *   fa_fwd     O = softmax(scale * Q K^T) V with the per-row log-sum-exp, by IO-aware
+ *              tiles and an online softmax (running max m, running sum l, rescaled fp32
+ *              accumulator, one division by l at the end).
+ *              Pages: V2/V3 article (aiqz.cc), sections "IO瓶颈分析", "V2算法优化" and
+ *              "Warp级并行"; interview answer "flash attention呢" (agentalpha.top),
+ *              标准答 part 1; study card airsota.com/?p=1562, sections 三 and 四 ①.
+ *   fa_bwd     dQ, dK, dV from dO, recomputing the local scores from Q, K and the saved
+ *              log-sum-exp instead of storing P.
+ *              Pages: interview answer 标准答 part 2 (recompute); study card section
+ *              四 ②; self-test page "二十四：Flash Attention自测题", section D (the dV,
+ *              dP, dS, dQ, dK relations).
+ *   fa_decode  one new token per sequence over a variable-length KV cache: the cache
+ *              is cut into chunks attended independently (partial O and LSE), then the
+ *              partials are merged by the online-softmax update.
+ *              Pages: interview answer, 高频追问 2; self-test page, section F.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  * Tensors are [batch, heads, seq, dim] (self-test page section A; the article's
+ *    Python demo), addressed by element strides for the batch, head and sequence
+ *    dimensions; the dim dimension is contiguous (stride 1).  Strides and base
+ *    pointers must keep every row 16-byte aligned.
+ *  * MHA / GQA / MQA: Hq query heads, Hkv key/value heads, Hq % Hkv == 0; query head
+ *    h reads KV head h / (Hq / Hkv) (self-test page section F).
+ *  * scale multiplies Q K^T before the softmax; callers normally pass 1/sqrt(D)
+ *    (self-test page section C; study card section 二).  It must be > 0 and finite.
+ *  * causal: key j is visible to query i iff j <= i + (Lk - Nq), Lk being the number
+ *    of valid keys of that batch entry (lower-triangular for Nq == Lk; the last query
+ *    sees the whole cache).
+ *  * Variable-length KV: keys at positions >= Lk do not exist.  Their memory is never
+ *    read into a result (it may hold NaN).  A query row with no visible key gets
+ *    O = 0 and LSE = -inf, and zero gradients.
+ *  * LSE is natural-log, in the units of the scaled scores: LSE_i = m_i + ln(l_i).
+ *  * Every pointer named "device" is device memory owned by the caller; the library
+ *    never allocates, frees or synchronises, keeps no mutable global state and is
+ *    safe to call from several host threads.  Work is enqueued asynchronously on the
+ *    caller's HIP stream (`stream` is a hipStream_t; NULL means the null stream);
+ *    outputs are valid once that stream reaches the enqueued work.
+ *  * Validation runs on the host before anything is enqueued: a non-FA_OK return
+ *    means nothing was launched and no output was touched.  FA_ERR_LAUNCH reports a
+ *    launch failure from the HIP runtime.  No C++ exception crosses this ABI.
+ *  * Device code is built for gfx950 only; fa_device_supported() says whether a
+ *    device can run it.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL_PTR = 1,    /* a required pointer is NULL                         */
+  FA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent              */
+  FA_ERR_DTYPE = 3,       /* unknown or unsupported dtype combination            */
+  FA_ERR_STRIDE = 4,      /* a stride or pointer breaks the 16-byte alignment    */
+  FA_ERR_UNSUPPORTED = 5, /* valid request this build does not implement (e.g. D) */
+  FA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the query says       */
+  FA_ERR_DEVICE = 7,      /* no current HIP device, or it is not gfx950          */
+  FA_ERR_LAUNCH = 8,      /* the HIP runtime rejected a kernel launch            */
+  FA_ERR_ARG = 9          /* scale not finite and > 0, or another bad scalar     */
+} fa_status;
+
+typedef enum fa_dtype {
+  FA_BF16 = 0,
+  FA_F32 = 1
+} fa_dtype;
+
+/* ---------------------------------------------------------------------------------
+ * Forward.
+ *   q  [B, Hq,  Nq, D]  in_dtype  (device)
+ *   k  [B, Hkv, Nk, D]  in_dtype  (device)
+ *   v  [B, Hkv, Nk, D]  in_dtype  (device)
+ *   o  [B, Hq,  Nq, D]  out_dtype (device, written)
+ *   lse  contiguous [B, Hq, Nq] fp32 (device, written), or NULL if not wanted
+ *   kv_lens  [B] int32 (device), valid keys per batch entry (clamped to [0, Nk]), or
+ *            NULL meaning Nk for every entry
+ *   k and v may be NULL when Nk == 0 (nothing is read).
+ * Supported: in_dtype FA_BF16 with D in {64, 128} and out_dtype FA_BF16 or FA_F32;
+ *            in_dtype FA_F32 with D = 64 and out_dtype FA_F32.
+ * Sizes: B, Hq, Hkv >= 1; Nq, Nk >= 0 (Nq == 0 launches nothing).  Nk == 0 or an
+ *        all-zero kv_lens gives O = 0, LSE = -inf.
+ * ------------------------------------------------------------------------------- */
+typedef struct fa_fwd_args {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const int32_t *kv_lens;
+  int64_t q_stride[3]; /* elements: batch, head, seq */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  int32_t B, Hq, Hkv, Nq, Nk, D;
+  int32_t in_dtype;  /* fa_dtype */
+  int32_t out_dtype; /* fa_dtype */
+  float scale;
+  int32_t causal;    /* 0 or 1 */
+} fa_fwd_args;
+
+fa_status fa_fwd(const fa_fwd_args *args, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Backward (bf16, D in {64, 128}).
+ *   q, k, v, o, dout  as in the forward (o is the forward output, dout = dL/dO), bf16
+ *   lse   contiguous [B, Hq, Nq] fp32, natural log, as written by fa_fwd (device)
+ *   dq    [B, Hq,  Nq, D] bf16 (device, written)
+ *   dk    [B, Hkv, Nk, D] bf16 (device, written; GQA: summed over the group's query
+ *         heads in fp32 before rounding)
+ *   dv    [B, Hkv, Nk, D] bf16 (device, written)
+ *   kv_lens, scale, causal as in the forward; rows of dk/dv at positions >= Lk are 0.
+ * The workspace (device, caller-owned, at least fa_bwd_workspace_bytes() bytes, any
+ * contents) holds D_i = rowsum(dO * O) [B, Hq, Nq] fp32 and the fp32 dQ accumulator
+ * [B, Hq, Nq, D]; it is initialised by the call itself.  Three kernels run in stream
+ * order: D_i (and accumulator clear), the dK/dV tile kernel with fp32 dQ atomics, and
+ * the dQ conversion.  dQ is not bitwise reproducible run to run (atomic order).
+ * ------------------------------------------------------------------------------- */
+typedef struct fa_bwd_args {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  void *dq, *dk, *dv;
+  const int32_t *kv_lens;
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  int64_t do_stride[3];
+  int64_t dq_stride[3];
+  int64_t dk_stride[3];
+  int64_t dv_stride[3];
+  int32_t B, Hq, Hkv, Nq, Nk, D;
+  int32_t dtype; /* FA_BF16 */
+  float scale;
+  int32_t causal;
+} fa_bwd_args;
+
+/* Bytes of workspace fa_bwd needs for these sizes (0 if the sizes are invalid). */
+size_t fa_bwd_workspace_bytes(const fa_bwd_args *args);
+fa_status fa_bwd(const fa_bwd_args *args, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Split-KV decode (bf16 cache, D in {64, 128}).
+ *   q        [Bs, Hq, D] bf16 (device), one new token per sequence
+ *   k_cache  [Bs, Hkv, cache_len, D] bf16 (device)
+ *   v_cache  [Bs, Hkv, cache_len, D] bf16 (device)
+ *   seq_lens [Bs] int32 (device): valid cached keys of each sequence; values are
+ *            clamped to [0, max_len] on the device
+ *   o        [Bs, Hq, D] out_dtype (device, written)
+ *   lse      contiguous [Bs, Hq] fp32 (device, written) or NULL
+ *   max_len  host-side bound on seq_lens, 0 <= max_len <= cache_len; sizes the grid
+ *            so no device-to-host copy is needed
+ *   split_len keys per chunk, a positive multiple of 128; chunk c of sequence s covers
+ *            keys [c*split_len, min((c+1)*split_len, L_s)).
+ * The workspace (device, at least fa_decode_workspace_bytes() bytes) receives each
+ * chunk's partial output and LSE, [Bs, Hq, ceil(max_len/split_len)] x (D + 1) fp32;
+ * a second kernel merges them:
+ *   M = max_c LSE_c, w_c = exp(LSE_c - M), O = sum_c w_c O_c / sum_c w_c,
+ *   LSE = M + ln(sum_c w_c).
+ * A sequence with L_s = 0 gets O = 0, LSE = -inf.
+ * ------------------------------------------------------------------------------- */
+typedef struct fa_decode_args {
+  const void *q;
+  const void *k_cache, *v_cache;
+  const int32_t *seq_lens;
+  void *o;
+  float *lse;
+  int64_t q_stride[2]; /* elements: sequence, head */
+  int64_t k_stride[3]; /* elements: sequence, head, position */
+  int64_t v_stride[3];
+  int64_t o_stride[2];
+  int32_t Bs, Hq, Hkv, D;
+  int32_t cache_len;
+  int32_t max_len;
+  int32_t split_len;
+  int32_t in_dtype;  /* FA_BF16 */
+  int32_t out_dtype; /* FA_BF16 or FA_F32 */
+  float scale;
+} fa_decode_args;
+
+size_t fa_decode_workspace_bytes(const fa_decode_args *args);
+fa_status fa_decode(const fa_decode_args *args, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *fa_status_str(int status);
+
+/* 1 if HIP device `device` is a gfx950 part this library was built for, else 0.
+ * Makes HIP runtime calls. */
+int fa_device_supported(int device);
+
+/* Library ABI version: (major << 16) | minor. */
+int fa_version(void);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,70 @@
+// fa_common.h -- device helpers shared by the gfx950 attention kernels.
+//
+// Vector types, the bf16 MFMA used for both attention contractions, bf16 packing,
+// cross-half-wave exchange, and the XCD-aware workgroup order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16) on the matrix cores.
+// Operand layout (wave64): lane l supplies row (A) / column (B) l % 32 and eight
+// consecutive k-elements of half l / 32.  Result: lane l holds column l % 32, and
+// register r holds row 8*(r/4) + 4*(l/32) + r%4.
+__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Two floats -> packed bf16 pair (round to nearest even); `lo` in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v = (bf16x2_t){(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// max / sum of the values held by lanes l and l ^ 32.  The swap returns the lane's own
+// value and the other half's value as its two results; a symmetric combine of both
+// does not depend on which result is which.
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup order: the dispatcher hands consecutive workgroup ids to the 8 XCDs in
+// turn.  Remap so that each XCD receives one contiguous range of logical tiles
+// (tiles that share K/V then share that XCD's L2).  A bijection on [0, total).
+__device__ __forceinline__ int xcd_contiguous(int id, int total) {
+  const int x = id % kNumXcd, k = id / kNumXcd;
+  const int q = total / kNumXcd, r = total % kNumXcd;
+  return x * q + (x < r ? x : r) + k;
+}
+
+__device__ __forceinline__ const uint16_t* as_u16(const void* p) {
+  return static_cast<const uint16_t*>(p);
+}
+
+}  // namespace fa

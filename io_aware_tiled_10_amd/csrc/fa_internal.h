@@ -1,0 +1,60 @@
+// fa_internal.h -- kernel parameter blocks and launchers behind the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Forward.  Strides are in elements; the dim dimension is contiguous.
+struct FwdParams {
+  const uint16_t* q;  // bf16 bits (or fp32 reinterpreted by the fp32 kernel)
+  const uint16_t* k;
+  const uint16_t* v;
+  void* o;
+  float* lse;
+  const int32_t* kv_lens;
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
+  int B, Hq, Hkv, Nq, Nk, G, nqt;
+  float scale, scale_log2;
+  int causal;
+};
+
+hipError_t launch_fwd(const FwdParams& p, int in_dtype, int out_dtype, int D, hipStream_t stream);
+
+// Backward.
+struct BwdParams {
+  const uint16_t *q, *k, *v, *o, *dout;
+  const float* lse;
+  uint16_t *dq, *dk, *dv;
+  const int32_t* kv_lens;
+  float* delta;   // [B, Hq, Nq] workspace
+  float* dq_acc;  // [B, Hq, Nq, D] workspace
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2, dos0, dos1, dos2;
+  int64_t dqs0, dqs1, dqs2, dks0, dks1, dks2, dvs0, dvs1, dvs2;
+  int B, Hq, Hkv, Nq, Nk, G, nkt;
+  float scale, scale_log2;
+  int causal;
+};
+
+size_t bwd_workspace_bytes(int B, int Hq, int Nq, int D);
+hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t stream);
+
+// Split-KV decode.
+struct DecParams {
+  const uint16_t* q;
+  const uint16_t *k, *v;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse;
+  float* part_o;    // [Bs, Hq, nsplit, D]
+  float* part_lse;  // [Bs, Hq, nsplit]
+  int64_t qs0, qs1, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1;
+  int Bs, Hq, Hkv, G, nhb, max_len, split_len, nsplit;
+  float scale, scale_log2;
+};
+
+size_t decode_workspace_bytes(int Bs, int Hq, int nsplit, int D);
+hipError_t launch_decode(const DecParams& p, int D, int out_dtype, hipStream_t stream);
+
+}  // namespace fa

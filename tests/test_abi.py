@@ -1,0 +1,160 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and its host-side validation rejects bad arguments with the
+documented status codes before anything is launched.
+
+Validation makes no HIP call, so these run on a machine without a GPU; no call
+here reaches a kernel launch (every argument block is invalid in some way).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from io_aware_tiled_10_amd import binding as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fb._LIB_PATH), reason="libfa.so not built")
+
+OK, NULL, SHAPE, DTYPE, STRIDE, UNSUP, WS, DEV, LAUNCH, ARG = range(10)
+FAKE = 0x7F0000000000  # a 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_calls():
+    assert declared_functions() == sorted(fb.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    h = fb.lib()
+    for name in declared_functions():
+        assert hasattr(h, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fb._LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(fa_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings_and_version():
+    h = fb.lib()
+    for s in range(10):
+        assert h.fa_status_str(s).decode().startswith("FA_")
+    assert h.fa_status_str(1234).decode() == "FA_ERR_UNKNOWN"
+    assert h.fa_version() >> 16 == 1
+
+
+def good_fwd(**kw):
+    a = fb.FwdArgs(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, kv_lens=None,
+                   q_stride=fb.c_i64x3(2 * 8 * 128, 8 * 128, 128), k_stride=fb.c_i64x3(2 * 8 * 128, 8 * 128, 128),
+                   v_stride=fb.c_i64x3(2 * 8 * 128, 8 * 128, 128), o_stride=fb.c_i64x3(2 * 8 * 128, 8 * 128, 128),
+                   B=1, Hq=2, Hkv=1, Nq=8, Nk=8, D=128, in_dtype=fb.FA_BF16, out_dtype=fb.FA_BF16,
+                   scale=0.088, causal=0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+FWD_BAD = [
+    ({"B": 0}, SHAPE), ({"Hq": 3, "Hkv": 2}, SHAPE), ({"Hkv": 4}, SHAPE), ({"Nq": -1}, SHAPE),
+    ({"Nk": -2}, SHAPE), ({"D": 96}, UNSUP), ({"D": 256}, UNSUP),
+    ({"in_dtype": 7}, DTYPE), ({"out_dtype": 9}, DTYPE),
+    ({"in_dtype": fb.FA_F32, "out_dtype": fb.FA_BF16}, DTYPE),
+    ({"in_dtype": fb.FA_F32, "out_dtype": fb.FA_F32, "D": 128}, UNSUP),
+    ({"scale": 0.0}, ARG), ({"scale": -1.0}, ARG), ({"scale": float("inf")}, ARG),
+    ({"scale": float("nan")}, ARG), ({"causal": 2}, ARG),
+    ({"q": None}, NULL), ({"k": None}, NULL), ({"v": None}, NULL), ({"o": None}, NULL),
+    ({"q": FAKE + 2}, STRIDE), ({"o": FAKE + 8}, STRIDE),
+    ({"q_stride": fb.c_i64x3(2 * 8 * 128, 8 * 128, 100)}, STRIDE),
+    ({"k_stride": fb.c_i64x3(-1, 8 * 128, 128)}, STRIDE),
+    ({"lse": FAKE + 2}, STRIDE),
+]
+
+
+@pytest.mark.parametrize("change,status", FWD_BAD)
+def test_fwd_rejects_bad_arguments(change, status):
+    a = good_fwd(**change)
+    assert fb.lib().fa_fwd(ctypes.byref(a), None) == status
+
+
+def test_fwd_null_args_and_empty_query():
+    assert fb.lib().fa_fwd(None, None) == NULL
+    # Nq == 0 is a valid request that launches nothing
+    assert fb.lib().fa_fwd(ctypes.byref(good_fwd(Nq=0)), None) == OK
+
+
+def good_bwd(**kw):
+    st = fb.c_i64x3(2 * 8 * 128, 8 * 128, 128)
+    a = fb.BwdArgs(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+                   kv_lens=None, q_stride=st, k_stride=st, v_stride=st, o_stride=st, do_stride=st,
+                   dq_stride=st, dk_stride=st, dv_stride=st, B=1, Hq=2, Hkv=2, Nq=8, Nk=8, D=128,
+                   dtype=fb.FA_BF16, scale=0.088, causal=1)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+BWD_BAD = [
+    ({"dtype": fb.FA_F32}, DTYPE), ({"D": 32}, UNSUP), ({"Hq": 3}, SHAPE),
+    ({"lse": None}, NULL), ({"dq": None}, NULL), ({"dk": None}, NULL), ({"dout": None}, NULL),
+    ({"dv": FAKE + 4}, STRIDE), ({"do_stride": fb.c_i64x3(0, 0, 3)}, STRIDE),
+    ({"scale": 0.0}, ARG), ({"causal": -1}, ARG),
+]
+
+
+@pytest.mark.parametrize("change,status", BWD_BAD)
+def test_bwd_rejects_bad_arguments(change, status):
+    a = good_bwd(**change)
+    assert fb.lib().fa_bwd(ctypes.byref(a), FAKE, 1 << 30, None) == status
+    assert fb.lib().fa_bwd_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def test_bwd_workspace_query_and_too_small_workspace():
+    a = good_bwd(B=2, Hq=16, Hkv=16, Nq=4096, Nk=4096)
+    need = fb.lib().fa_bwd_workspace_bytes(ctypes.byref(a))
+    rows = 2 * 16 * 4096
+    assert need == rows * 4 + rows * 128 * 4
+    assert fb.lib().fa_bwd(ctypes.byref(a), FAKE, need - 1, None) == WS
+    assert fb.lib().fa_bwd(ctypes.byref(a), None, need, None) == WS
+    assert fb.lib().fa_bwd(ctypes.byref(a), FAKE + 4, need, None) == WS
+
+
+def good_dec(**kw):
+    a = fb.DecodeArgs(q=FAKE, k_cache=FAKE, v_cache=FAKE, seq_lens=FAKE, o=FAKE, lse=FAKE,
+                      q_stride=fb.c_i64x2(32 * 128, 128), k_stride=fb.c_i64x3(8 * 4096 * 128, 4096 * 128, 128),
+                      v_stride=fb.c_i64x3(8 * 4096 * 128, 4096 * 128, 128), o_stride=fb.c_i64x2(32 * 128, 128),
+                      Bs=4, Hq=32, Hkv=8, D=128, cache_len=4096, max_len=4096, split_len=2048,
+                      in_dtype=fb.FA_BF16, out_dtype=fb.FA_BF16, scale=0.088)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+DEC_BAD = [
+    ({"max_len": 5000}, SHAPE), ({"split_len": 100}, SHAPE), ({"split_len": 0}, SHAPE),
+    ({"Hq": 30}, SHAPE), ({"Bs": -1}, SHAPE), ({"Bs": 70000}, SHAPE), ({"D": 80}, UNSUP),
+    ({"in_dtype": fb.FA_F32}, DTYPE), ({"out_dtype": 5}, DTYPE), ({"seq_lens": None}, NULL),
+    ({"k_cache": None}, NULL), ({"q": FAKE + 2}, STRIDE), ({"scale": -0.5}, ARG),
+]
+
+
+@pytest.mark.parametrize("change,status", DEC_BAD)
+def test_decode_rejects_bad_arguments(change, status):
+    a = good_dec(**change)
+    assert fb.lib().fa_decode(ctypes.byref(a), FAKE, 1 << 30, None) == status
+
+
+def test_decode_workspace_query():
+    a = good_dec(Bs=64, max_len=4096, cache_len=32768)
+    need = fb.lib().fa_decode_workspace_bytes(ctypes.byref(a))
+    rows = 64 * 32 * 2
+    assert need == rows * 128 * 4 + rows * 4
+    assert fb.lib().fa_decode(ctypes.byref(a), FAKE, need - 1, None) == WS
+    assert fb.lib().fa_decode(ctypes.byref(good_dec(Bs=0)), None, 0, None) == OK

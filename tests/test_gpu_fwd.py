@@ -1,0 +1,169 @@
+"""GPU parity of fa_fwd against the fp64 oracle (element by element).
+
+Tolerances: O max-abs <= 1e-2 (plus half a bf16 ulp of the reference when O is
+written in bf16) and LSE max-abs <= 1e-3, both for bf16 inputs; the same for the
+fp32 path.  Inputs are the seeded draws of io_aware_tiled_10_amd.inputs, given to
+both sides bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_tiled_10_amd as fa
+import oracle
+from io_aware_tiled_10_amd import inputs
+from tests.helpers import DEV, assert_fwd_close, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # name, B, Hq, Hkv, Nq, Nk, D, causal, kv_lens
+    ("mha_ragged_noncausal_d128", 2, 2, 2, 300, 300, 128, False, None),
+    ("mha_ragged_causal_d128", 2, 2, 2, 300, 300, 128, True, None),
+    ("gqa_causal_d128", 1, 8, 2, 257, 257, 128, True, None),
+    ("mqa_noncausal_d64", 1, 4, 1, 200, 333, 64, False, None),
+    ("causal_nq_lt_nk", 1, 2, 1, 100, 333, 128, True, None),
+    ("causal_nq_gt_nk_masked_rows", 1, 2, 2, 200, 70, 128, True, None),
+    ("kvlens_noncausal", 3, 2, 1, 130, 300, 128, False, [300, 1, 0]),
+    ("kvlens_causal_d64", 2, 4, 2, 150, 260, 64, True, [17, 259]),
+    ("single_row_single_key", 1, 1, 1, 1, 1, 128, False, None),
+    ("single_row_causal", 1, 2, 1, 1, 129, 128, True, None),
+    ("exact_tiles", 1, 2, 2, 256, 256, 128, True, None),
+]
+
+
+def run_case(B, Hq, Hkv, Nq, Nk, D, causal, kv_lens, out_dtype, seed=0, poison=False):
+    x = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, D, "bf16", seed=seed)
+    q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
+    kl = None
+    if kv_lens is not None:
+        kl = torch.tensor(kv_lens, dtype=torch.int32, device=DEV)
+        if poison:
+            for b, L in enumerate(kv_lens):
+                k[b, :, L:] = float("nan")
+                v[b, :, L:] = float("nan")
+    o, lse = fa.fwd(q, k, v, causal=causal, kv_lens=kl, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(x.q, x.k, x.v, None, causal, kv_lens)
+    return to_host(o), to_host(lse), o_ref, lse_ref
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["oF32", "oBF16"])
+def test_fwd_bf16_matches_oracle(case, out_dtype):
+    name, B, Hq, Hkv, Nq, Nk, D, causal, kv_lens = case
+    say(f"fwd case {name} out={out_dtype}")
+    o, lse, o_ref, lse_ref = run_case(B, Hq, Hkv, Nq, Nk, D, causal, kv_lens, out_dtype)
+    err = assert_fwd_close(o, lse, o_ref, lse_ref, out_dtype == torch.bfloat16)
+    say(f"  max|dO| = {err:.3e}")
+    if out_dtype == torch.float32:
+        # fp32 output: only bf16 rounding of P separates the kernel from exact
+        assert err < 4e-3
+
+
+def test_fwd_nan_poisoned_padding_is_never_read():
+    say("fwd poisoned padding")
+    o, lse, o_ref, lse_ref = run_case(2, 4, 2, 96, 300, 128, True, [77, 300], torch.float32, poison=True)
+    assert_fwd_close(o, lse, o_ref, lse_ref, False)
+
+
+def test_fwd_fp32_config_c1():
+    # fp32 B1 H2 N256 D64 non-causal, full oracle comparison
+    say("fwd fp32 c1")
+    x = inputs.attention_inputs(1, 2, 2, 256, 256, 64, "fp32", seed=0)
+    q, k, v = (to_dev(a, torch.float32) for a in (x.q, x.k, x.v))
+    o, lse = fa.fwd(q, k, v, causal=False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(x.q, x.k, x.v)
+    err = assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, False)
+    assert err < 1e-5, err
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp32_ragged(causal):
+    x = inputs.attention_inputs(2, 2, 1, 100, 150, 64, "fp32", seed=3)
+    q, k, v = (to_dev(a, torch.float32) for a in (x.q, x.k, x.v))
+    o, lse = fa.fwd(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(x.q, x.k, x.v, None, causal)
+    assert assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, False) < 1e-5
+
+
+def test_fwd_gqa_equals_mha_with_repeated_kv():
+    x = inputs.attention_inputs(1, 8, 2, 200, 200, 128, "bf16", seed=5)
+    q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
+    o1, l1 = fa.fwd(q, k, v, causal=True, out_dtype=torch.float32)
+    kr, vr = k.repeat_interleave(4, dim=1), v.repeat_interleave(4, dim=1)
+    o2, l2 = fa.fwd(q, kr, vr, causal=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fwd_strided_layout_bnhd():
+    # [B, N, H, D] memory (the flash-attn layout) passed through strides
+    x = inputs.attention_inputs(2, 4, 2, 130, 130, 128, "bf16", seed=6)
+    qn = to_dev(x.q).transpose(1, 2).contiguous().transpose(1, 2)
+    kn = to_dev(x.k).transpose(1, 2).contiguous().transpose(1, 2)
+    vn = to_dev(x.v).transpose(1, 2).contiguous().transpose(1, 2)
+    o, lse = fa.fwd(qn, kn, vn, causal=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(x.q, x.k, x.v, None, True)
+    assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, False)
+
+
+def test_fwd_is_deterministic():
+    x = inputs.attention_inputs(1, 4, 1, 513, 513, 128, "bf16", seed=7)
+    q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
+    a = fa.fwd(q, k, v, causal=True)
+    b = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_fwd_empty_key_set_gives_zero_and_neg_inf():
+    x = inputs.attention_inputs(1, 2, 2, 40, 0, 128, "bf16", seed=8)
+    q = to_dev(x.q)
+    k = torch.zeros((1, 2, 0, 128), dtype=torch.bfloat16, device=DEV)  # may carry a NULL pointer
+    o, lse = fa.fwd(q, k, k, causal=False, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+# --------------------------------------------------------------------------------------
+# full-size workloads, launched as the benchmark launches them; sampled rows vs oracle
+# --------------------------------------------------------------------------------------
+
+FULL = [
+    ("c2_noncausal", 4, 16, 16, 2048, 128, False),
+    ("c2_causal", 4, 16, 16, 2048, 128, True),
+    ("c3_gqa_causal_16k", 1, 32, 8, 16384, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", FULL, ids=[c[0] for c in FULL])
+def test_fwd_full_size_sampled_rows(case):
+    name, B, Hq, Hkv, N, D, causal = case
+    say(f"fwd full {name}")
+    x = inputs.attention_inputs(B, Hq, Hkv, N, N, D, "bf16", seed=0)
+    q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
+    o, lse = fa.fwd(q, k, v, causal=causal)              # bf16 O, as timed
+    o32, lse32 = fa.fwd(q, k, v, causal=causal, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, N - 1], rng.integers(0, N, 27)]))
+    rt = torch.from_numpy(rows).to(DEV)
+    heads = sorted(set([0, Hq - 1] + list(rng.integers(0, Hq, 3))))
+    bs = sorted(set([0, B - 1]))
+    for b in bs:
+        for h in heads:
+            o_ref, lse_ref = oracle.attn_fwd(x.q[b:b + 1, h:h + 1], x.k[b:b + 1, h // (Hq // Hkv):h // (Hq // Hkv) + 1],
+                                             x.v[b:b + 1, h // (Hq // Hkv):h // (Hq // Hkv) + 1], None, causal,
+                                             rows=rows)
+            assert_fwd_close(to_host(o32[b, h, rt])[None, None], to_host(lse32[b, h, rt])[None, None],
+                             o_ref, lse_ref, False)
+            assert_fwd_close(to_host(o[b, h, rt])[None, None], to_host(lse[b, h, rt])[None, None],
+                             o_ref, lse_ref, True)
+    # properties that hold at any size: finite outputs, LSE agreement of both dtypes
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    assert torch.equal(lse, lse32)
