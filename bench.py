@@ -194,6 +194,8 @@ def main():
     ap.add_argument("--legs", default="fwd,bwd,decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--aux", action="store_true", help="also time the B4 H16 N2048 forwards")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 256 MiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -273,6 +275,14 @@ def main():
             out_legs[name] = {"ms": round(ms, 4), "tflops": round(tf, 2),
                               "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "in_step": False}
             del leg
+
+    if args.calib_copy:
+        src = torch.empty(128 << 20, dtype=torch.bfloat16, device=DEV).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize()
+        del src, dst
 
     value = flops / (ms_per_step * 1e-3) / 1e12
     roofline = None

@@ -67,4 +67,20 @@ __device__ __forceinline__ const uint16_t* as_u16(const void* p) {
   return static_cast<const uint16_t*>(p);
 }
 
+// Raw buffer resource over [base, base + bytes): a 16-byte load whose offset lies past
+// the end returns zeros, so rows beyond a valid length need no branch and no select.
+// 0x00020000 is the gfx9-family third descriptor word for untyped 32-bit data.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// Bytes a buffer over `rows` rows of `pitch_bytes` must span so that every 16-byte
+// chunk of each of those rows (width row_bytes) is in range and the next row is not.
+__device__ __forceinline__ uint32_t rows_span(int rows, int64_t pitch_bytes, int row_bytes) {
+  return rows <= 0 ? 0u : (uint32_t)((int64_t)(rows - 1) * pitch_bytes + row_bytes);
+}
+
 }  // namespace fa

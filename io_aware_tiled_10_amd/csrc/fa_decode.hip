@@ -44,8 +44,7 @@ struct DecTile {
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int CPR = D / 8;           // 16-byte chunks per cached row
-  static constexpr int NQ = 64 / CPR;         // 4-key quads covered by one pass of the wave
-  static constexpr int NG = kDecBlock / (4 * NQ);  // passes per 32-key block
+  static constexpr int NG = CPR / 8;          // column passes: 8 columns x 8 key quads each
   static constexpr int VT_LD = kDecBlock + 8;
   static constexpr int VT_ELEMS = D * VT_LD;   // per wave (bf16)
   static constexpr int MRG_FLOATS = 64 + D * 32;  // per merged wave: m, l, acc
@@ -55,12 +54,13 @@ struct DecTile {
 };
 
 template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_split_kernel(DecParams p) {
   using T = DecTile<D>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[T::LDS_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar descriptors
   const int l32 = lane & 31, hi = lane >> 5;
   const int c = blockIdx.x, s = blockIdx.z;
   const int hkv = blockIdx.y / p.nhb, hb = blockIdx.y % p.nhb;
@@ -86,37 +86,41 @@ decode_split_kernel(DecParams p) {
   }
   const uint16_t* kb = p.k + s * p.ks0 + hkv * p.ks1;
   const uint16_t* vb = p.v + s * p.vs0 + hkv * p.vs1;
+  const int64_t kpitch = p.ks2 * 2, vpitch = p.vs2 * 2;
   uint16_t* vt = reinterpret_cast<uint16_t*>(lds) + wave * T::VT_ELEMS;
-  const int vcol = lane % T::CPR, qd = lane / T::CPR;
+  // V staging: lanes 8j..8j+7 hold the 8 four-key groups of one 16-byte column, so the
+  // transposed writes of 8 lanes fill one 32-key V^T row.
+  const int vq = lane % 8, vcol0 = lane / 8;
   const float cl = p.scale_log2;
+  const uint32_t koff = (uint32_t)(l32 * kpitch) + 16 * hi;
+  const uint32_t voff = (uint32_t)(4 * vq * vpitch) + 16 * vcol0;
 
   f32x16_t acc[T::DB];
 #pragma unroll
   for (int d = 0; d < T::DB; ++d) acc[d] = f32x16_t{};
   float m = -INFINITY, l = 0.f;
 
-  for (int blk = wave; blk < nb; blk += kDecWaves) {
+  // keys of this wave's block n: [start + 32 (wave + 4 n), ...); out-of-chunk rows read 0
+  u32x4_t ka[2][T::KS], vr[2][T::NG][4];
+  auto load = [&](int buf, int blk) {
     const int key0 = start + blk * kDecBlock;
-    u32x4_t ka[T::KS], vr[T::NG][4];
-    {
-      const int key = key0 + l32;
-      const uint16_t* krow = kb + (int64_t)key * p.ks2 + 8 * hi;
+    const int rows = min(kDecBlock, end - key0);
+    const auto rk = make_rsrc(kb + (int64_t)key0 * p.ks2, rows_span(rows, kpitch, D * 2));
+    const auto rv = make_rsrc(vb + (int64_t)key0 * p.vs2, rows_span(rows, vpitch, D * 2));
 #pragma unroll
-      for (int k = 0; k < T::KS; ++k)
-        ka[k] = key < end ? *reinterpret_cast<const u32x4_t*>(krow + 16 * k) : zero4;
-    }
+    for (int k = 0; k < T::KS; ++k) ka[buf][k] = buf_load16(rk, koff + 32 * k);
 #pragma unroll
     for (int g = 0; g < T::NG; ++g)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = key0 + 4 * (g * T::NQ + qd) + i;
-        vr[g][i] = key < end ? *reinterpret_cast<const u32x4_t*>(vb + (int64_t)key * p.vs2 + 8 * vcol)
-                             : zero4;
-      }
+      for (int i = 0; i < 4; ++i)
+        vr[buf][g][i] = buf_load16(rv, voff + (uint32_t)(i * vpitch) + 16 * (T::CPR / T::NG) * g);
+  };
 
+  auto step = [&](int buf, int blk) {
+    const int key0 = start + blk * kDecBlock;
     f32x16_t sc{};
 #pragma unroll
-    for (int k = 0; k < T::KS; ++k) sc = mfma32(ka[k], qf[k], sc);
+    for (int k = 0; k < T::KS; ++k) sc = mfma32(ka[buf][k], qf[k], sc);
     if (key0 + kDecBlock > end) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -126,8 +130,8 @@ decode_split_kernel(DecParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
     mx = halves_max(mx);
-    const float m_new = fmaxf(m, mx);  // finite: every block holds a valid key
-    const float alpha = fast_exp2((m - m_new) * cl);
+    const float m_new = fmaxf(m, mx);  // finite: the wave's first block holds a valid key
+    const float alpha = fast_exp2((m - m_new) * cl);  // 0 on the first block, 1 if empty
     const float mc = m_new * cl;
     u32x4_t pf[2];
     float rs = 0.f;
@@ -146,11 +150,13 @@ decode_split_kernel(DecParams p) {
     wave_lds_order();
 #pragma unroll
     for (int g = 0; g < T::NG; ++g) {
-      const int pos = vt_pos16(4 * (g * T::NQ + qd));
+      const int pos = vt_pos16(4 * vq);
+      const int dcol = 8 * (vcol0 + (T::CPR / T::NG) * g);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t x0 = vr[g][0][w], x1 = vr[g][1][w], x2 = vr[g][2][w], x3 = vr[g][3][w];
-        uint16_t* even = vt + (8 * vcol + 2 * w) * T::VT_LD + pos;
+        const uint32_t x0 = vr[buf][g][0][w], x1 = vr[buf][g][1][w], x2 = vr[buf][g][2][w],
+                       x3 = vr[buf][g][3][w];
+        uint16_t* even = vt + (dcol + 2 * w) * T::VT_LD + pos;
         *reinterpret_cast<u32x2_t*>(even) =
             u32x2_t{(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
         *reinterpret_cast<u32x2_t*>(even + T::VT_LD) =
@@ -167,6 +173,23 @@ decode_split_kernel(DecParams p) {
         acc[d] = mfma32(a, pf[ts], acc[d]);
       }
     wave_lds_order();
+  };
+
+  // Software pipeline: the wave's next block is in flight while the current one
+  // computes.  Loads are unconditional (a block past the chunk has a zero-length
+  // descriptor and reads zeros without touching memory) and the trip count is rounded
+  // up to even; a trailing empty step leaves (m, l, acc) unchanged since every score
+  // is -inf.  Waves without a block skip the loop.
+  const int mine = wave < nb ? (nb - wave + kDecWaves - 1) / kDecWaves : 0;
+  if (mine > 0) {
+    load(0, wave);
+    for (int n = 0; n < mine; n += 2) {
+      const int b0 = wave + kDecWaves * n;
+      load(1, b0 + kDecWaves);
+      step(0, b0);
+      load(0, b0 + 2 * kDecWaves);
+      step(1, b0 + kDecWaves);
+    }
   }
   l = halves_sum(l);
 

@@ -52,6 +52,13 @@ __device__ __forceinline__ int vt_pos(int k) {
   return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
 }
 
+// The running maximum used as the exponent reference is only moved when a block's
+// maximum exceeds it by more than this many powers of two (per-wave decision).  Until
+// then probabilities may exceed 1 by at most 2^kLazyRescale, which bf16 P and the fp32
+// sums absorb; the final O = acc / l and LSE = m*scale + ln(l) use the same reference,
+// so the result is unchanged while almost every accumulator rescale is skipped.
+constexpr float kLazyRescale = 8.f;
+
 template <int D, bool OUT_F32>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_bf16_kernel(FwdParams p) {
@@ -89,39 +96,60 @@ fwd_bf16_kernel(FwdParams p) {
   const int nblk = (kend + BC - 1) / BC;
 
   const int qi = q_wg0 + wave * 32 + l32;  // this lane's query row
-  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
 
-  // ---- Q^T fragments (B operand), loaded once
+  if (nblk == 0) {  // no visible key for any row of the tile: O = 0, LSE = -inf
+    if (qi < p.Nq) {
+      if constexpr (OUT_F32) {
+        float* orow = static_cast<float*>(p.o) + b * p.os0 + hq * p.os1 + (int64_t)qi * p.os2;
+        for (int d = 4 * hi; d < D; d += 8) *reinterpret_cast<f32x4_t*>(orow + d) = f32x4_t{};
+      } else {
+        uint16_t* orow = static_cast<uint16_t*>(p.o) + b * p.os0 + hq * p.os1 + (int64_t)qi * p.os2;
+        for (int d = 4 * hi; d < D; d += 8) *reinterpret_cast<u32x2_t*>(orow + d) = u32x2_t{};
+      }
+      if (p.lse && hi == 0) p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qi] = -INFINITY;
+    }
+    return;  // uniform over the workgroup
+  }
+
+  // ---- Q^T fragments (B operand), loaded once; rows past Nq read as zero
   u32x4_t qf[T::KS];
   {
-    const uint16_t* qrow = p.q + b * p.qs0 + hq * p.qs1 + (int64_t)qi * p.qs2;
+    const int64_t qpitch = p.qs2 * 2;
+    const uint16_t* qtile = p.q + b * p.qs0 + hq * p.qs1 + (int64_t)q_wg0 * p.qs2;
+    const auto rq = make_rsrc(qtile, rows_span(min(BR, p.Nq - q_wg0), qpitch, D * 2));
+    const uint32_t off = (uint32_t)((wave * 32 + l32) * qpitch) + 16 * hi;
 #pragma unroll
-    for (int s = 0; s < T::KS; ++s)
-      qf[s] = qi < p.Nq ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * s + 8 * hi) : zero4;
+    for (int s = 0; s < T::KS; ++s) qf[s] = buf_load16(rq, off + 32 * s);
   }
 
   const uint16_t* kbase = p.k + b * p.ks0 + hkv * p.ks1;
   const uint16_t* vbase = p.v + b * p.vs0 + hkv * p.vs1;
-  const int vcol = tid % T::CPR;
-  const int vk0 = T::KPT * (tid / T::CPR);
+  const int64_t kpitch = p.ks2 * 2, vpitch = p.vs2 * 2;
+  // K staging: chunk c = tid + 256 i -> (row c / CPR, column c % CPR), coalesced rows.
+  // V staging: lanes sharing a column hold consecutive 4-key (2-key) groups, so the
+  // transposed LDS writes of 16 lanes cover one V^T row without bank conflicts.
+  constexpr int VG = BC / T::KPT;  // key groups per block
+  const int vkg = tid % VG, vcol = tid / VG;
+  const int vk0 = T::KPT * vkg;
+  uint32_t koff[T::KCH];
+#pragma unroll
+  for (int i = 0; i < T::KCH; ++i) {
+    const int c = tid + 256 * i;
+    koff[i] = (uint32_t)((c / T::CPR) * kpitch) + 16 * (c % T::CPR);
+  }
+  const uint32_t voff = (uint32_t)(vk0 * vpitch) + 16 * vcol;
 
   u32x4_t kreg[T::KCH], vreg[T::KPT];
 
   auto load_block = [&](int blk) {
     const int key0 = blk * BC;
+    const int rows = min(BC, lk - key0);
+    const auto rk = make_rsrc(kbase + (int64_t)key0 * p.ks2, rows_span(rows, kpitch, D * 2));
+    const auto rv = make_rsrc(vbase + (int64_t)key0 * p.vs2, rows_span(rows, vpitch, D * 2));
 #pragma unroll
-    for (int i = 0; i < T::KCH; ++i) {
-      const int c = tid + 256 * i, row = c / T::CPR, col = c % T::CPR;
-      const int key = key0 + row;
-      kreg[i] = key < lk ? *reinterpret_cast<const u32x4_t*>(kbase + (int64_t)key * p.ks2 + 8 * col)
-                         : zero4;
-    }
+    for (int i = 0; i < T::KCH; ++i) kreg[i] = buf_load16(rk, koff[i]);
 #pragma unroll
-    for (int i = 0; i < T::KPT; ++i) {
-      const int key = key0 + vk0 + i;
-      vreg[i] = key < lk ? *reinterpret_cast<const u32x4_t*>(vbase + (int64_t)key * p.vs2 + 8 * vcol)
-                         : zero4;
-    }
+    for (int i = 0; i < T::KPT; ++i) vreg[i] = buf_load16(rv, voff + (uint32_t)(i * vpitch));
   };
 
   auto store_block = [&](int st) {
@@ -154,13 +182,12 @@ fwd_bf16_kernel(FwdParams p) {
   f32x16_t acc[T::DB];
 #pragma unroll
   for (int d = 0; d < T::DB; ++d) acc[d] = f32x16_t{};
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f;  // m: exponent reference (raw score units)
   const float c = p.scale_log2;
+  const float thresh = kLazyRescale / c;
 
-  if (nblk > 0) {
-    load_block(0);
-    store_block(0);
-  }
+  load_block(0);
+  store_block(0);
   __syncthreads();
 
   for (int j = 0; j < nblk; ++j) {
@@ -196,10 +223,16 @@ fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
     mx = halves_max(mx);
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2((m - m_use) * c);
-    const float mc = m_use * c;
+    // move the reference only when some row of the wave grew past the threshold
+    if (__builtin_amdgcn_ballot_w64(mx > m + thresh || (m == -INFINITY && mx != -INFINITY))) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = m == -INFINITY ? 0.f : fast_exp2((m - m_new) * c);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < T::DB; ++d) acc[d] *= alpha;
+      m = m_new;
+    }
+    const float mc = (m == -INFINITY ? 0.f : m) * c;
 
     u32x4_t pf[4];
     float rs = 0.f;
@@ -211,11 +244,8 @@ fwd_bf16_kernel(FwdParams p) {
       pf[r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
       pf[2 + (r >> 3)][(r & 7) >> 1] = pack_bf16(p2, p3);
     }
-    l = l * alpha + rs;
-    m = m_new;
+    l += rs;
 
-#pragma unroll
-    for (int d = 0; d < T::DB; ++d) acc[d] *= alpha;
 #pragma unroll
     for (int d = 0; d < T::DB; ++d) {
 #pragma unroll
