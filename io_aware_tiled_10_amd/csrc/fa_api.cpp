@@ -105,6 +105,7 @@ fa_status validate_decode(const fa_decode_args* a) {
   if (!scale_ok(a->scale)) return FA_ERR_ARG;
   const int64_t nhb = (a->Hq / a->Hkv + 31) / 32;
   if ((int64_t)a->Hkv * nhb > kMaxGridYZ) return FA_ERR_SHAPE;
+  if ((int64_t)decode_nsplit(a) * nhb * a->Hkv * a->Bs > 0x7fffffff) return FA_ERR_SHAPE;
   if (a->Bs == 0) return FA_OK;
   if (!a->q || !a->o || !a->seq_lens) return FA_ERR_NULL_PTR;
   if (a->max_len > 0 && (!a->k_cache || !a->v_cache)) return FA_ERR_NULL_PTR;

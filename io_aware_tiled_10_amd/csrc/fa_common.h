@@ -76,6 +76,52 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+// The same load marked non-temporal (cache policy bit "nt"): for data read exactly once,
+// such as a KV cache streamed by the decode, so it does not displace reused lines.
+__device__ __forceinline__ u32x4_t buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
+
+// Direct global -> LDS load (gfx950 LDS DMA): lane t's 16 bytes, read at byte `off` of
+// the buffer, land at lds + 16 t; the register file is bypassed.  Out-of-range bytes are
+// written as zeros.  `lds` must be the same for the whole wave.  The compiler does not
+// track these writes: the issuing code waits with wait_vmcnt before reading them.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off,
+                                          int aux = 0) {
+  if (aux)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                             (int)off, 0, 0, 2);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                             (int)off, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding; also a
+// compiler barrier for memory accesses.
+#define FA_WAIT_VMCNT(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
+#define FA_WAIT_LGKMCNT0() asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory")
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16) of 4 bf16 values per lane.  Within
+// each group of 16 lanes, let M be the 16 x 4 matrix whose row i is the 8 bytes at lane
+// i's address; lane j receives M[j/4 + 4e][j%4] for e = 0..3, packed two per dword.
+// Issued from inline assembly so that the compiler neither waits for unrelated LDS-DMA
+// loads before it nor tracks its completion: the caller must run lds_wait_tr on the
+// results before using them.  Two reads at byte offsets O0 and O1 from `addr`.
+template <int O0, int O1>
+__device__ __forceinline__ void lds_read_tr16x2(u32x2_t& a, u32x2_t& b, uint32_t addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
+               : "=&v"(a), "=&v"(b)
+               : "v"(addr), "i"(O0), "i"(O1));
+}
+// Wait for all outstanding LDS reads of this wave; the operands tie the results of
+// earlier lds_read_tr16x2 calls to this point, so no use of them moves above the wait.
+__device__ __forceinline__ void lds_wait_tr(u32x2_t& a, u32x2_t& b, u32x2_t& c, u32x2_t& d) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d)::"memory");
+}
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
 // Bytes a buffer over `rows` rows of `pitch_bytes` must span so that every 16-byte
 // chunk of each of those rows (width row_bytes) is in range and the next row is not.

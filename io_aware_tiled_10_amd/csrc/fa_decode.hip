@@ -14,9 +14,14 @@
 //  * one workgroup per (chunk, KV head, sequence), so every cached K/V byte is read
 //    from HBM exactly once and shared by the query heads of its GQA group, which
 //    occupy the 32 columns of the MFMA tile (padding columns are zero queries);
-//  * each of the 4 waves walks its own 32-key blocks of the chunk (no workgroup
-//    barrier in the streaming loop); keys feed S^T = K q^T straight from global
-//    memory, V goes through a per-wave transposed LDS tile for O^T += V^T P^T;
+//  * each of the 4 waves walks its own 32-key blocks of the chunk with no workgroup
+//    barrier: the blocks stream straight from HBM into a private two-stage LDS ring
+//    (LDS DMA, no registers), one fully coalesced, non-temporal 1 KiB load per
+//    instruction, so the next block is in flight while the current one computes;
+//  * the 16-byte slots of each LDS row are XOR-swizzled on the way in so that the
+//    MFMA operand reads are free of bank conflicts: K rows feed S^T = K q^T with plain
+//    16-byte reads, V feeds O^T += V^T P^T through transposing reads (no register
+//    shuffles and no second LDS pass);
 //  * the four waves' (m, l, acc) are merged through LDS at the end of the chunk;
 //  * chunks past a sequence's length exit at once; keys past it are never loaded.
 #include "fa_common.h"
@@ -29,41 +34,42 @@ namespace {
 constexpr int kDecWaves = 4;
 constexpr int kDecBlock = 32;  // keys per wave step
 
-__device__ __forceinline__ int vt_pos16(int k) {
-  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
-}
-
-__device__ __forceinline__ void wave_lds_order() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <int D>
 struct DecTile {
-  static constexpr int KS = D / 16;
-  static constexpr int DB = D / 32;
-  static constexpr int CPR = D / 8;           // 16-byte chunks per cached row
-  static constexpr int NG = CPR / 8;          // column passes: 8 columns x 8 key quads each
-  static constexpr int VT_LD = kDecBlock + 8;
-  static constexpr int VT_ELEMS = D * VT_LD;   // per wave (bf16)
+  static constexpr int KS = D / 16;               // k-steps of S^T = K q^T
+  static constexpr int DB = D / 32;               // 32-row blocks of O^T
+  static constexpr int ROWB = D * 2;              // bytes per cached row
+  static constexpr int SPR = D / 8;               // 16-byte slots per row
+  static constexpr int RPB = 256 / ROWB;          // rows per 256-byte LDS bank period
+  static constexpr int TBYTES = kDecBlock * ROWB; // one tensor (K or V) of a block
+  static constexpr int NDMA = TBYTES / 1024;      // 1 KiB DMA instructions per tensor
+  static constexpr int RPI = 1024 / ROWB;         // rows per DMA instruction
+  static constexpr int STAGE = 2 * TBYTES;        // K then V
+  static constexpr int RING = 2 * STAGE;          // two stages per wave
   static constexpr int MRG_FLOATS = 64 + D * 32;  // per merged wave: m, l, acc
-  static constexpr int VT_BYTES = kDecWaves * VT_ELEMS * 2;
+  static constexpr int RING_BYTES = kDecWaves * RING;
   static constexpr int MRG_BYTES = (kDecWaves - 1) * MRG_FLOATS * 4;
-  static constexpr int LDS_BYTES = VT_BYTES > MRG_BYTES ? VT_BYTES : MRG_BYTES;
+  static constexpr int LDS_BYTES = RING_BYTES > MRG_BYTES ? RING_BYTES : MRG_BYTES;
+  // slot swizzles (row r of a staged block): K rows are read 16 at a time at one logical
+  // slot, V rows 8 at a time over 4 consecutive slots (transposing reads)
+  static __device__ __forceinline__ int swz_k(int r) { return (r / RPB) % SPR; }
+  static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPB) % (SPR / 4)); }
 };
 
 template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-decode_split_kernel(DecParams p) {
+__global__ void __launch_bounds__(256) decode_split_kernel(DecParams p) {
   using T = DecTile<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[T::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[T::LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar descriptors
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
   const int l32 = lane & 31, hi = lane >> 5;
-  const int c = blockIdx.x, s = blockIdx.z;
-  const int hkv = blockIdx.y / p.nhb, hb = blockIdx.y % p.nhb;
+  // Workgroup id = pair + npair * chunk, (head block, KV head, sequence) fastest: the
+  // dispatcher deals consecutive ids to the 8 XCDs in turn, so every XCD receives the
+  // same mix of chunk positions.
+  const int npair = p.nhb * p.Hkv * p.Bs;
+  const int pair = (int)(blockIdx.x % (unsigned)npair), c = (int)(blockIdx.x / (unsigned)npair);
+  const int hb = pair % p.nhb, hkv = (pair / p.nhb) % p.Hkv, s = pair / (p.nhb * p.Hkv);
 
   int L = p.seq_lens[s];
   L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
@@ -75,121 +81,128 @@ decode_split_kernel(DecParams p) {
   const int gh = hb * 32 + l32;  // head within the GQA group held by this lane's column
   const bool hvalid = gh < p.G;
   const int hq = hkv * p.G + gh;
-  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
 
+  // q of the group's heads through one descriptor: columns past the group read zeros
+  // (unconditional loads keep the compiler's memory-counter bookkeeping exact)
   u32x4_t qf[T::KS];
   {
-    const uint16_t* qrow = p.q + s * p.qs0 + (int64_t)hq * p.qs1;
+    const auto rq = make_rsrc(p.q + s * p.qs0 + (int64_t)hkv * p.G * p.qs1,
+                              rows_span(p.G, p.qs1 * 2, D * 2));
+    const uint32_t off = (uint32_t)(gh * p.qs1 * 2) + 16 * hi;
 #pragma unroll
-    for (int k = 0; k < T::KS; ++k)
-      qf[k] = hvalid ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * k + 8 * hi) : zero4;
+    for (int k = 0; k < T::KS; ++k) qf[k] = buf_load16(rq, off + 32 * k);
+    asm volatile("" ::: "memory");  // issue these before the ring loads below
   }
   const uint16_t* kb = p.k + s * p.ks0 + hkv * p.ks1;
   const uint16_t* vb = p.v + s * p.vs0 + hkv * p.vs1;
   const int64_t kpitch = p.ks2 * 2, vpitch = p.vs2 * 2;
-  uint16_t* vt = reinterpret_cast<uint16_t*>(lds) + wave * T::VT_ELEMS;
-  // V staging: lanes 8j..8j+7 hold the 8 four-key groups of one 16-byte column, so the
-  // transposed writes of 8 lanes fill one 32-key V^T row.
-  const int vq = lane % 8, vcol0 = lane / 8;
-  const float cl = p.scale_log2;
-  const uint32_t koff = (uint32_t)(l32 * kpitch) + 16 * hi;
-  const uint32_t voff = (uint32_t)(4 * vq * vpitch) + 16 * vcol0;
+  unsigned char* ring = lds + wave * T::RING;
+
+  // DMA instruction i writes staged rows RPI*i ..; lane t fills slot t % SPR of row
+  // RPI*i + t / SPR with the swizzled chunk of that row
+  uint32_t kdma[T::NDMA], vdma[T::NDMA];
+#pragma unroll
+  for (int i = 0; i < T::NDMA; ++i) {
+    const int r = T::RPI * i + lane / T::SPR, slot = lane % T::SPR;
+    kdma[i] = (uint32_t)(r * kpitch) + 16 * (slot ^ T::swz_k(r));
+    vdma[i] = (uint32_t)(r * vpitch) + 16 * (slot ^ T::swz_v(r));
+  }
+  // S^T operand reads: row l32, logical slot 2k + hi
+  const int krow = l32 * T::ROWB, ksw = T::swz_k(l32);
+  // V^T operand reads (transposing): lane 16g + i reads row 16 ts + 8 r + 4 (g/2) + i/4,
+  // columns 32 db + 16 (g%2) + 4 (i%4) .. +3; the row's swizzle depends only on i.
+  const int vg = lane >> 4, vi = lane & 15;
+  const int vrow = 4 * (vg >> 1) + (vi >> 2);
+  const int vlo = 2 * (vg & 1) + ((vi & 3) >> 1);      // slot within the 4-slot group
+  const int vsw = T::swz_v(vrow) >> 2;                // group swizzle
+  const int vbase = vrow * T::ROWB + 16 * vlo + 8 * (vi & 1);
 
   f32x16_t acc[T::DB];
 #pragma unroll
   for (int d = 0; d < T::DB; ++d) acc[d] = f32x16_t{};
   float m = -INFINITY, l = 0.f;
+  const float cl = p.scale_log2;
 
-  // keys of this wave's block n: [start + 32 (wave + 4 n), ...); out-of-chunk rows read 0
-  u32x4_t ka[2][T::KS], vr[2][T::NG][4];
-  auto load = [&](int buf, int blk) {
-    const int key0 = start + blk * kDecBlock;
+  // block n of this wave covers keys [start + 32 (wave + 4 n), +32); past the chunk the
+  // descriptor is empty, nothing is read and the stage is filled with zeros
+  auto issue = [&](int n) {
+    const int key0 = start + kDecBlock * (wave + kDecWaves * n);
     const int rows = min(kDecBlock, end - key0);
-    const auto rk = make_rsrc(kb + (int64_t)key0 * p.ks2, rows_span(rows, kpitch, D * 2));
-    const auto rv = make_rsrc(vb + (int64_t)key0 * p.vs2, rows_span(rows, vpitch, D * 2));
+    const auto rk = make_rsrc(kb + (int64_t)key0 * p.ks2, rows_span(rows, kpitch, T::ROWB));
+    const auto rv = make_rsrc(vb + (int64_t)key0 * p.vs2, rows_span(rows, vpitch, T::ROWB));
+    unsigned char* st = ring + (n & 1) * T::STAGE;
 #pragma unroll
-    for (int k = 0; k < T::KS; ++k) ka[buf][k] = buf_load16(rk, koff + 32 * k);
+    for (int i = 0; i < T::NDMA; ++i) lds_dma16(rk, st + 1024 * i, kdma[i], 1);
 #pragma unroll
-    for (int g = 0; g < T::NG; ++g)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vr[buf][g][i] = buf_load16(rv, voff + (uint32_t)(i * vpitch) + 16 * (T::CPR / T::NG) * g);
+    for (int i = 0; i < T::NDMA; ++i) lds_dma16(rv, st + T::TBYTES + 1024 * i, vdma[i], 1);
   };
 
-  auto step = [&](int buf, int blk) {
-    const int key0 = start + blk * kDecBlock;
-    f32x16_t sc{};
-#pragma unroll
-    for (int k = 0; k < T::KS; ++k) sc = mfma32(ka[buf][k], qf[k], sc);
-    if (key0 + kDecBlock > end) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (key0 + 8 * (r >> 2) + 4 * hi + (r & 3) >= end) sc[r] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-    mx = halves_max(mx);
-    const float m_new = fmaxf(m, mx);  // finite: the wave's first block holds a valid key
-    const float alpha = fast_exp2((m - m_new) * cl);  // 0 on the first block, 1 if empty
-    const float mc = m_new * cl;
-    u32x4_t pf[2];
-    float rs = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = fast_exp2(fmaf(sc[r], cl, -mc)), p1 = fast_exp2(fmaf(sc[r + 1], cl, -mc));
-      rs += p0 + p1;
-      pf[r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
-    }
-    l = l * alpha + rs;
-    m = m_new;
-#pragma unroll
-    for (int d = 0; d < T::DB; ++d) acc[d] *= alpha;
-
-    // V^T tile of this wave, keys permuted to the score register order
-    wave_lds_order();
-#pragma unroll
-    for (int g = 0; g < T::NG; ++g) {
-      const int pos = vt_pos16(4 * vq);
-      const int dcol = 8 * (vcol0 + (T::CPR / T::NG) * g);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x0 = vr[buf][g][0][w], x1 = vr[buf][g][1][w], x2 = vr[buf][g][2][w],
-                       x3 = vr[buf][g][3][w];
-        uint16_t* even = vt + (dcol + 2 * w) * T::VT_LD + pos;
-        *reinterpret_cast<u32x2_t*>(even) =
-            u32x2_t{(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
-        *reinterpret_cast<u32x2_t*>(even + T::VT_LD) =
-            u32x2_t{(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
-      }
-    }
-    wave_lds_order();
-#pragma unroll
-    for (int d = 0; d < T::DB; ++d)
-#pragma unroll
-      for (int ts = 0; ts < 2; ++ts) {
-        const u32x4_t a =
-            *reinterpret_cast<const u32x4_t*>(vt + (32 * d + l32) * T::VT_LD + 16 * ts + 8 * hi);
-        acc[d] = mfma32(a, pf[ts], acc[d]);
-      }
-    wave_lds_order();
-  };
-
-  // Software pipeline: the wave's next block is in flight while the current one
-  // computes.  Loads are unconditional (a block past the chunk has a zero-length
-  // descriptor and reads zeros without touching memory) and the trip count is rounded
-  // up to even; a trailing empty step leaves (m, l, acc) unchanged since every score
-  // is -inf.  Waves without a block skip the loop.
   const int mine = wave < nb ? (nb - wave + kDecWaves - 1) / kDecWaves : 0;
   if (mine > 0) {
-    load(0, wave);
-    for (int n = 0; n < mine; n += 2) {
-      const int b0 = wave + kDecWaves * n;
-      load(1, b0 + kDecWaves);
-      step(0, b0);
-      load(0, b0 + 2 * kDecWaves);
-      step(1, b0 + kDecWaves);
+    issue(0);
+    issue(1);
+    for (int n = 0; n < mine; ++n) {
+      // block n landed; the 2 * NDMA loads of block n + 1 may still be in flight
+      if constexpr (T::NDMA == 8) FA_WAIT_VMCNT(16); else FA_WAIT_VMCNT(8);
+      static_assert(T::NDMA == 8 || T::NDMA == 4, "wait count below assumes D = 128 or 64");
+      const unsigned char* ks = ring + (n & 1) * T::STAGE;
+      const unsigned char* vs = ks + T::TBYTES;
+      const int key0 = start + kDecBlock * (wave + kDecWaves * n);
+
+      f32x16_t sc{};
+#pragma unroll
+      for (int k = 0; k < T::KS; ++k) {
+        const u32x4_t a =
+            *reinterpret_cast<const u32x4_t*>(ks + krow + 16 * ((2 * k + hi) ^ ksw));
+        sc = mfma32(a, qf[k], sc);
+      }
+      if (key0 + kDecBlock > end) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + 8 * (r >> 2) + 4 * hi + (r & 3) >= end) sc[r] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+      mx = halves_max(mx);
+      const float m_new = fmaxf(m, mx);  // finite: each computed block holds a valid key
+      const float alpha = fast_exp2((m - m_new) * cl);  // 0 on the first block
+      const float mc = m_new * cl;
+      u32x4_t pf[2];
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(fmaf(sc[r], cl, -mc)), p1 = fast_exp2(fmaf(sc[r + 1], cl, -mc));
+        rs += p0 + p1;
+        pf[r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
+      }
+      l = l * alpha + rs;
+      m = m_new;
+
+      // O^T += V^T P^T; k-step ts holds keys 16 ts + 8 (e/4) + 4 hi + e%4 (e = 0..7), the
+      // register order of the scores, which the transposing reads reproduce
+      u32x2_t vt[T::DB][2][2];
+      const uint32_t va = lds_addr(vs) + vbase;
+#pragma unroll
+      for (int d = 0; d < T::DB; ++d) {
+        const uint32_t a = va + 64 * (d ^ vsw);
+        lds_read_tr16x2<0, 8 * T::ROWB>(vt[d][0][0], vt[d][0][1], a);
+        lds_read_tr16x2<16 * T::ROWB, 24 * T::ROWB>(vt[d][1][0], vt[d][1][1], a);
+      }
+#pragma unroll
+      for (int d = 0; d < T::DB; ++d) lds_wait_tr(vt[d][0][0], vt[d][0][1], vt[d][1][0], vt[d][1][1]);
+#pragma unroll
+      for (int d = 0; d < T::DB; ++d) {
+        acc[d] *= alpha;
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts)
+          acc[d] = mfma32(u32x4_t{vt[d][ts][0][0], vt[d][ts][0][1], vt[d][ts][1][0], vt[d][ts][1][1]},
+                          pf[ts], acc[d]);
+      }
+      FA_WAIT_LGKMCNT0();  // every read of this stage has returned
+      issue(n + 2);
     }
+    FA_WAIT_VMCNT(0);  // the trailing (empty) loads write the ring too
   }
   l = halves_sum(l);
 
@@ -299,7 +312,9 @@ size_t decode_workspace_bytes(int Bs, int Hq, int nsplit, int D) {
 
 hipError_t launch_decode(const DecParams& p, int D, int out_dtype, hipStream_t stream) {
   if (p.nsplit > 0) {
-    const dim3 grid(p.nsplit, p.Hkv * p.nhb, p.Bs);
+    const int64_t n = (int64_t)p.nsplit * p.nhb * p.Hkv * p.Bs;
+    if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)n);
     const hipError_t e = D == 128 ? launch(decode_split_kernel<128>, grid, dim3(256), p, stream)
                                   : launch(decode_split_kernel<64>, grid, dim3(256), p, stream);
     if (e != hipSuccess) return e;
