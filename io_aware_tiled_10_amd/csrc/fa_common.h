@@ -87,19 +87,23 @@ __device__ __forceinline__ u32x4_t buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint3
 // written as zeros.  `lds` must be the same for the whole wave.  The compiler does not
 // track these writes: the issuing code waits with wait_vmcnt before reading them.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off,
-                                          int aux = 0) {
+                                          int aux = 0, int soff = 0) {
   if (aux)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                             (int)off, 0, 0, 2);
+                                             (int)off, soff, 0, 2);
   else
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                             (int)off, 0, 0, 0);
+                                             (int)off, soff, 0, 0);
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding; also a
 // compiler barrier for memory accesses.
 #define FA_WAIT_VMCNT(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
 #define FA_WAIT_LGKMCNT0() asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory")
+// Workgroup barrier without the memory fence __syncthreads() adds (which waits for every
+// outstanding load, ring prefetches included).  Callers order LDS themselves: each wave
+// waits for its own ring loads (FA_WAIT_VMCNT) and LDS reads (lgkmcnt) before it.
+#define FA_BARRIER() asm volatile("s_barrier" ::: "memory")
 
 // gfx950 transposing LDS read (ds_read_b64_tr_b16) of 4 bf16 values per lane.  Within
 // each group of 16 lanes, let M be the 16 x 4 matrix whose row i is the 8 bytes at lane
@@ -111,7 +115,8 @@ template <int O0, int O1>
 __device__ __forceinline__ void lds_read_tr16x2(u32x2_t& a, u32x2_t& b, uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
                : "=&v"(a), "=&v"(b)
-               : "v"(addr), "i"(O0), "i"(O1));
+               : "v"(addr), "i"(O0), "i"(O1)
+               : "memory");
 }
 // Wait for all outstanding LDS reads of this wave; the operands tie the results of
 // earlier lds_read_tr16x2 calls to this point, so no use of them moves above the wait.

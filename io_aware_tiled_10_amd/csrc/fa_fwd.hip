@@ -8,16 +8,24 @@
 // probability tiles never leave the chip.
 //
 // gfx950 mapping of the bf16 kernel (a redesign, not the pages' A100/H100 layout):
-//  * one workgroup = 4 waves = 128 query rows; each wave owns 32 rows outright (the
-//    article's "Warp级并行" principle: no reduction across waves);
-//  * a K/V block is 64 keys; K is staged row-major and V transposed into LDS, double
-//    buffered: the global loads of block j+1 are in flight while block j computes;
+//  * one workgroup = 8 waves = 256 query rows, one workgroup per compute unit (two
+//    waves per SIMD); each wave owns 32 rows outright (the article's "Warp级并行"
+//    principle: no reduction across waves).  A K/V block staged in LDS serves all 256
+//    rows, halving the L2 -> LDS traffic per FLOP against 128-row tiles;
+//  * K/V blocks of 64 keys go from L2/HBM straight into LDS (LDS DMA: coalesced 1 KiB
+//    per wave instruction, no staging registers) through three-slot rings, with the
+//    16-byte slots of every row XOR-swizzled so that the operand reads are free of
+//    bank conflicts.  K runs one block ahead of V; each load has two blocks of compute
+//    to land, and one barrier per block orders the ring;
 //  * the scores are computed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMA, so each
 //    lane holds one query's scores: the row max / sum are lane-local plus a single
 //    exchange between the two wave halves;
-//  * the probabilities stay in registers as the B operand of O^T += V^T P^T; V^T is
-//    stored with its keys permuted to match the score register order, so no shuffle
-//    is needed between the two products;
+//  * software pipeline inside each wave: the MFMAs of the next block's scores are
+//    issued together with the exp / rescale work of the current block, which only
+//    needs the vector units;
+//  * the probabilities stay in registers as the B operand of O^T += V^T P^T; the V^T
+//    operand comes from transposing LDS reads (ds_read_b64_tr_b16) in the key order of
+//    the score registers, so no shuffle is needed between the two products;
 //  * exp is exp2 with scale*log2(e) folded into one fma per score;
 //  * causal: blocks above the diagonal are never visited, the mask is applied only
 //    on blocks that cross it, and the heaviest query tiles are launched first;
@@ -29,28 +37,26 @@ namespace fa {
 
 namespace {
 
-constexpr int kFwdBR = 128;  // query rows per workgroup
-constexpr int kFwdBC = 64;   // keys per block
+constexpr int kFwdWaves = 8;
+constexpr int kFwdBR = 32 * kFwdWaves;  // query rows per workgroup
+constexpr int kFwdBC = 64;              // keys per block
+constexpr int kFwdSlots = 3;            // ring depth for K and for V
 
 template <int D>
 struct FwdTile {
-  static constexpr int KS = D / 16;            // k-steps of S^T = K Q^T
-  static constexpr int DB = D / 32;            // 32-row blocks of O^T
-  static constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
-  static constexpr int KCH = kFwdBC * CPR / 256;  // K chunks per thread
-  static constexpr int KPT = KCH;              // V keys per thread (8 dims each)
-  static constexpr int K_LD = D + 8;           // LDS row pitch of K (elements)
-  static constexpr int V_LD = kFwdBC + 8;      // LDS row pitch of V^T (elements)
-  static constexpr int STAGE = kFwdBC * K_LD + D * V_LD;
+  static constexpr int KS = D / 16;              // k-steps of S^T = K Q^T
+  static constexpr int DB = D / 32;              // 32-row blocks of O^T
+  static constexpr int ROWB = D * 2;             // bytes per K/V row
+  static constexpr int SPR = D / 8;              // 16-byte slots per row
+  static constexpr int RPB = 256 / ROWB;         // rows per 256-byte LDS bank period
+  static constexpr int RPI = 1024 / ROWB;        // rows per wave DMA instruction
+  static constexpr int TBYTES = kFwdBC * ROWB;   // one K or V block in LDS
+  static constexpr int NDMA = TBYTES / (1024 * kFwdWaves);  // DMA instructions per thread
+  static constexpr int LDS_BYTES = 2 * kFwdSlots * TBYTES;
+  static_assert(NDMA * 1024 * kFwdWaves == TBYTES, "a block must split evenly over the waves");
+  static __device__ __forceinline__ int swz_k(int r) { return (r / RPB) % SPR; }
+  static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPB) % (SPR / 4)); }
 };
-
-// Position of key k (0..15 within its group of 16) in the transposed V tile.  The
-// MFMA result puts key 8a + 4h + b (a, h in {0,1}, b in 0..3) of a 16-key step in
-// wave half h, element 4a + b; storing it at 8h + 4a + b lets each lane fetch its
-// eight V^T elements with one 16-byte read.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
-}
 
 // The running maximum used as the exponent reference is only moved when a block's
 // maximum exceeds it by more than this many powers of two (per-wave decision).  Until
@@ -60,13 +66,16 @@ __device__ __forceinline__ int vt_pos(int k) {
 constexpr float kLazyRescale = 8.f;
 
 template <int D, bool OUT_F32>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64 * kFwdWaves) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_bf16_kernel(FwdParams p) {
   using T = FwdTile<D>;
-  constexpr int BR = kFwdBR, BC = kFwdBC;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE];
+  constexpr int BR = kFwdBR, BC = kFwdBC, NW = kFwdWaves, NS = kFwdSlots;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[T::LDS_BYTES];
+  unsigned char* kring = lds;
+  unsigned char* vring = lds + NS * T::TBYTES;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
   // ---- which tile: XCD-contiguous, KV-head-major, heavy causal tiles first
@@ -120,64 +129,59 @@ fwd_bf16_kernel(FwdParams p) {
     const uint32_t off = (uint32_t)((wave * 32 + l32) * qpitch) + 16 * hi;
 #pragma unroll
     for (int s = 0; s < T::KS; ++s) qf[s] = buf_load16(rq, off + 32 * s);
+    asm volatile("" ::: "memory");  // issue these before the ring loads below
   }
 
   const uint16_t* kbase = p.k + b * p.ks0 + hkv * p.ks1;
   const uint16_t* vbase = p.v + b * p.vs0 + hkv * p.vs1;
   const int64_t kpitch = p.ks2 * 2, vpitch = p.vs2 * 2;
-  // K staging: chunk c = tid + 256 i -> (row c / CPR, column c % CPR), coalesced rows.
-  // V staging: lanes sharing a column hold consecutive 4-key (2-key) groups, so the
-  // transposed LDS writes of 16 lanes cover one V^T row without bank conflicts.
-  constexpr int VG = BC / T::KPT;  // key groups per block
-  const int vkg = tid % VG, vcol = tid / VG;
-  const int vk0 = T::KPT * vkg;
-  uint32_t koff[T::KCH];
-#pragma unroll
-  for (int i = 0; i < T::KCH; ++i) {
-    const int c = tid + 256 * i;
-    koff[i] = (uint32_t)((c / T::CPR) * kpitch) + 16 * (c % T::CPR);
-  }
-  const uint32_t voff = (uint32_t)(vk0 * vpitch) + 16 * vcol;
 
-  u32x4_t kreg[T::KCH], vreg[T::KPT];
+  // DMA: thread (wave w, lane) fills, for instruction i, row RPI (NW i + w) + lane / SPR,
+  // slot lane % SPR, with the swizzled 16-byte chunk of that row; the swizzle of that
+  // row does not depend on i, and the row step of i goes into the scalar offset.
+  const int drow = T::RPI * wave + lane / T::SPR, dslot = lane % T::SPR;
+  const uint32_t kdma = (uint32_t)(drow * kpitch) + 16 * (dslot ^ T::swz_k(drow));
+  const uint32_t vdma = (uint32_t)(drow * vpitch) + 16 * (dslot ^ T::swz_v(drow));
+  const int kstep = (int)(NW * T::RPI * kpitch), vstep = (int)(NW * T::RPI * vpitch);
 
-  auto load_block = [&](int blk) {
+  auto dma_k = [&](int blk, int slot) {  // blocks past the keys fill the slot with zeros
     const int key0 = blk * BC;
-    const int rows = min(BC, lk - key0);
-    const auto rk = make_rsrc(kbase + (int64_t)key0 * p.ks2, rows_span(rows, kpitch, D * 2));
-    const auto rv = make_rsrc(vbase + (int64_t)key0 * p.vs2, rows_span(rows, vpitch, D * 2));
+    const auto rk = make_rsrc(kbase + (int64_t)key0 * p.ks2, rows_span(min(BC, lk - key0), kpitch, D * 2));
+    unsigned char* dst = kring + slot * T::TBYTES + 1024 * wave;
 #pragma unroll
-    for (int i = 0; i < T::KCH; ++i) kreg[i] = buf_load16(rk, koff[i]);
+    for (int i = 0; i < T::NDMA; ++i) lds_dma16(rk, dst + 1024 * NW * i, kdma, 0, kstep * i);
+  };
+  auto dma_v = [&](int blk, int slot) {
+    const int key0 = blk * BC;
+    const auto rv = make_rsrc(vbase + (int64_t)key0 * p.vs2, rows_span(min(BC, lk - key0), vpitch, D * 2));
+    unsigned char* dst = vring + slot * T::TBYTES + 1024 * wave;
 #pragma unroll
-    for (int i = 0; i < T::KPT; ++i) vreg[i] = buf_load16(rv, voff + (uint32_t)(i * vpitch));
+    for (int i = 0; i < T::NDMA; ++i) lds_dma16(rv, dst + 1024 * NW * i, vdma, 0, vstep * i);
   };
 
-  auto store_block = [&](int st) {
-    uint16_t* Ks = smem + st * T::STAGE;
-    uint16_t* Vs = Ks + BC * T::K_LD;
+  // S^T operand reads: rows l32 and 32 + l32 (same swizzle), logical slot 2 ks + hi
+  const int krow = l32 * T::ROWB, ksw = T::swz_k(l32);
+  auto qk = [&](int slot, f32x16_t& s0, f32x16_t& s1) {
+    const unsigned char* ks = kring + slot * T::TBYTES + krow;
+    s0 = f32x16_t{};
+    s1 = f32x16_t{};
 #pragma unroll
-    for (int i = 0; i < T::KCH; ++i) {
-      const int c = tid + 256 * i, row = c / T::CPR, col = c % T::CPR;
-      *reinterpret_cast<u32x4_t*>(Ks + row * T::K_LD + 8 * col) = kreg[i];
-    }
-    const int pos = vt_pos(vk0);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint16_t* even = Vs + (8 * vcol + 2 * w) * T::V_LD + pos;
-      uint16_t* odd = even + T::V_LD;
-      if constexpr (T::KPT == 4) {
-        const uint32_t x0 = vreg[0][w], x1 = vreg[1][w], x2 = vreg[2][w], x3 = vreg[3][w];
-        *reinterpret_cast<u32x2_t*>(even) =
-            u32x2_t{(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
-        *reinterpret_cast<u32x2_t*>(odd) =
-            u32x2_t{(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
-      } else {
-        const uint32_t x0 = vreg[0][w], x1 = vreg[1][w];
-        *reinterpret_cast<uint32_t*>(even) = (x0 & 0xffffu) | (x1 << 16);
-        *reinterpret_cast<uint32_t*>(odd) = (x0 >> 16) | (x1 & 0xffff0000u);
-      }
+    for (int k = 0; k < T::KS; ++k) {
+      const int o = 16 * ((2 * k + hi) ^ ksw);
+      const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(ks + o);
+      const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(ks + 32 * T::ROWB + o);
+      s0 = mfma32(a0, qf[k], s0);
+      s1 = mfma32(a1, qf[k], s1);
     }
   };
+
+  // V^T operand reads (transposing): lane 16 g + i reads row 16 ts + 8 r + 4 (g/2) + i/4,
+  // columns 32 db + 16 (g%2) + 4 (i%4) .. +3; the row's swizzle depends only on i.
+  const int vg = lane >> 4, vi = lane & 15;
+  const int vrow = 4 * (vg >> 1) + (vi >> 2);
+  const int vsw = T::swz_v(vrow) >> 2;
+  const uint32_t vlane = vrow * T::ROWB + 16 * (2 * (vg & 1) + ((vi & 3) >> 1)) + 8 * (vi & 1);
+  const uint32_t vring_addr = lds_addr(vring);
 
   f32x16_t acc[T::DB];
 #pragma unroll
@@ -186,26 +190,12 @@ fwd_bf16_kernel(FwdParams p) {
   const float c = p.scale_log2;
   const float thresh = kLazyRescale / c;
 
-  load_block(0);
-  store_block(0);
-  __syncthreads();
-
-  for (int j = 0; j < nblk; ++j) {
-    const int st = j & 1;
-    if (j + 1 < nblk) load_block(j + 1);
-    const uint16_t* Ks = smem + st * T::STAGE;
-    const uint16_t* Vs = Ks + BC * T::K_LD;
-
-    // S^T = K Q^T for keys [0,32) and [32,64) of the block
-    f32x16_t s0{}, s1{};
-#pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) {
-      const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(Ks + l32 * T::K_LD + 16 * ks + 8 * hi);
-      const u32x4_t a1 =
-          *reinterpret_cast<const u32x4_t*>(Ks + (32 + l32) * T::K_LD + 16 * ks + 8 * hi);
-      s0 = mfma32(a0, qf[ks], s0);
-      s1 = mfma32(a1, qf[ks], s1);
-    }
+  // One block: (s0, s1) hold the scores of block j (keys 64 j + [0, 32), + [32, 64));
+  // the scores of block j + 1 are produced into (n0, n1).
+  auto step = [&](int j, f32x16_t& s0, f32x16_t& s1, f32x16_t& n0, f32x16_t& n1) {
+    // K_{j+3} and V_{j+2} into the slots blocks j and j - 1 finished with
+    dma_k(j + 3, j % NS);
+    dma_v(j + 2, (j + 2) % NS);
 
     const int key0 = j * BC;
     const bool edge = (key0 + BC > lk) || (p.causal && key0 + BC - 1 > q_wg0 + diag);
@@ -221,7 +211,7 @@ fwd_bf16_kernel(FwdParams p) {
 
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
     mx = halves_max(mx);
     // move the reference only when some row of the wave grew past the threshold
     if (__builtin_amdgcn_ballot_w64(mx > m + thresh || (m == -INFINITY && mx != -INFINITY))) {
@@ -233,6 +223,10 @@ fwd_bf16_kernel(FwdParams p) {
       m = m_new;
     }
     const float mc = (m == -INFINITY ? 0.f : m) * c;
+
+    // next block's scores on the matrix cores while this block's exps run on the VALU
+    // (past the last block the slot holds zeros and the result is not used)
+    qk((j + 1) % NS, n0, n1);
 
     u32x4_t pf[4];
     float rs = 0.f;
@@ -246,19 +240,50 @@ fwd_bf16_kernel(FwdParams p) {
     }
     l += rs;
 
+    // O^T += V^T P^T; k-step ts holds keys 16 ts + 8 (e/4) + 4 hi + e%4 (e = 0..7)
+    const uint32_t va = vring_addr + (j % NS) * T::TBYTES + vlane;
 #pragma unroll
     for (int d = 0; d < T::DB; ++d) {
+      const uint32_t a = va + 64 * (d ^ vsw);
+      u32x2_t v[4][2];
+      lds_read_tr16x2<0, 8 * T::ROWB>(v[0][0], v[0][1], a);
+      lds_read_tr16x2<16 * T::ROWB, 24 * T::ROWB>(v[1][0], v[1][1], a);
+      lds_read_tr16x2<32 * T::ROWB, 40 * T::ROWB>(v[2][0], v[2][1], a);
+      lds_read_tr16x2<48 * T::ROWB, 56 * T::ROWB>(v[3][0], v[3][1], a);
+      lds_wait_tr(v[0][0], v[0][1], v[1][0], v[1][1]);
+      lds_wait_tr(v[2][0], v[2][1], v[3][0], v[3][1]);
 #pragma unroll
-      for (int ts = 0; ts < 4; ++ts) {
-        const u32x4_t a =
-            *reinterpret_cast<const u32x4_t*>(Vs + (32 * d + l32) * T::V_LD + 16 * ts + 8 * hi);
-        acc[d] = mfma32(a, pf[ts], acc[d]);
-      }
+      for (int ts = 0; ts < 4; ++ts)
+        acc[d] = mfma32(u32x4_t{v[ts][0][0], v[ts][0][1], v[ts][1][0], v[ts][1][1]}, pf[ts], acc[d]);
     }
 
-    if (j + 1 < nblk) store_block(st ^ 1);
-    __syncthreads();
+    // the loads of blocks j + 2 (K) and j + 1 (V), issued one block ago, have landed
+    // (only this block's may still be in flight); the barrier then publishes them and
+    // frees the slots this block read
+    if constexpr (T::NDMA == 2) FA_WAIT_VMCNT(4); else FA_WAIT_VMCNT(2);
+    FA_WAIT_LGKMCNT0();
+    FA_BARRIER();
+  };
+  static_assert(T::NDMA == 2 || T::NDMA == 1, "wait counts above assume D = 128 or 64");
+
+  dma_k(0, 0);
+  dma_k(1, 1);
+  dma_k(2, 2);
+  dma_v(0, 0);
+  dma_v(1, 1);
+  FA_WAIT_VMCNT(0);
+  __syncthreads();
+  f32x16_t sa0, sa1, sb0, sb1;
+  qk(0, sa0, sa1);
+  FA_WAIT_LGKMCNT0();  // K slot 0 is refilled at the top of the first block:
+  __syncthreads();     // every wave's reads of it must be done
+
+  int j = 0;
+  for (; j + 1 < nblk; j += 2) {  // two blocks per trip: the score registers alternate
+    step(j, sa0, sa1, sb0, sb1);
+    step(j + 1, sb0, sb1, sa0, sa1);
   }
+  if (j < nblk) step(j, sa0, sa1, sb0, sb1);
 
   // ---- epilogue: O = acc / l once; LSE = m * scale + ln(l)
   const float lt = halves_sum(l);
@@ -414,10 +439,10 @@ hipError_t launch_fwd(const FwdParams& p0, int in_dtype, int out_dtype, int D, h
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const bool of32 = out_dtype == FA_F32;
   if (D == 128)
-    return of32 ? launch(fwd_bf16_kernel<128, true>, (int)grid, 256, p, stream)
-                : launch(fwd_bf16_kernel<128, false>, (int)grid, 256, p, stream);
-  return of32 ? launch(fwd_bf16_kernel<64, true>, (int)grid, 256, p, stream)
-              : launch(fwd_bf16_kernel<64, false>, (int)grid, 256, p, stream);
+    return of32 ? launch(fwd_bf16_kernel<128, true>, (int)grid, 64 * kFwdWaves, p, stream)
+                : launch(fwd_bf16_kernel<128, false>, (int)grid, 64 * kFwdWaves, p, stream);
+  return of32 ? launch(fwd_bf16_kernel<64, true>, (int)grid, 64 * kFwdWaves, p, stream)
+              : launch(fwd_bf16_kernel<64, false>, (int)grid, 64 * kFwdWaves, p, stream);
 }
 
 }  // namespace fa
