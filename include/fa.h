@@ -118,8 +118,9 @@ fa_status fa_fwd(const fa_fwd_args *args, void *stream);
  *   dv    [B, Hkv, Nk, D] bf16 (device, written)
  *   kv_lens, scale, causal as in the forward; rows of dk/dv at positions >= Lk are 0.
  * The workspace (device, caller-owned, at least fa_bwd_workspace_bytes() bytes, any
- * contents) holds D_i = rowsum(dO * O) [B, Hq, Nq] fp32 and the fp32 dQ accumulator
- * [B, Hq, Nq, D]; it is initialised by the call itself.  Three kernels run in stream
+ * contents) holds, per query row, the pair (LSE * log2 e, D_i = rowsum(dO * O)) in
+ * fp32 [B, Hq, Nq, 2] and the fp32 dQ accumulator [B, Hq, Nq, D]; it is initialised
+ * by the call itself.  Three kernels run in stream
  * order: D_i (and accumulator clear), the dK/dV tile kernel with fp32 dQ atomics, and
  * the dQ conversion.  dQ is not bitwise reproducible run to run (atomic order).
  * ------------------------------------------------------------------------------- */

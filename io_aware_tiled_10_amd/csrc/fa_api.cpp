@@ -169,9 +169,6 @@ fa_status fa_bwd(const fa_bwd_args* a, void* workspace, size_t ws_bytes, void* s
   p.dk = static_cast<uint16_t*>(a->dk);
   p.dv = static_cast<uint16_t*>(a->dv);
   p.kv_lens = a->kv_lens;
-  const size_t delta_bytes = ((size_t)a->B * a->Hq * a->Nq * 4 + 255) & ~size_t(255);
-  p.delta = static_cast<float*>(workspace);
-  p.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes);
   p.qs0 = a->q_stride[0], p.qs1 = a->q_stride[1], p.qs2 = a->q_stride[2];
   p.ks0 = a->k_stride[0], p.ks1 = a->k_stride[1], p.ks2 = a->k_stride[2];
   p.vs0 = a->v_stride[0], p.vs1 = a->v_stride[1], p.vs2 = a->v_stride[2];
@@ -185,6 +182,7 @@ fa_status fa_bwd(const fa_bwd_args* a, void* workspace, size_t ws_bytes, void* s
   p.scale = a->scale;
   p.scale_log2 = a->scale * 1.4426950408889634f;
   p.causal = a->causal;
+  fa::bwd_bind_workspace(p, workspace, a->D);
   return map_launch_error(fa::launch_bwd(p, a->D, static_cast<hipStream_t>(stream)));
 }
 

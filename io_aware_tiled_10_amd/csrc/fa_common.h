@@ -118,6 +118,13 @@ __device__ __forceinline__ void lds_read_tr16x2(u32x2_t& a, u32x2_t& b, uint32_t
                : "v"(addr), "i"(O0), "i"(O1)
                : "memory");
 }
+template <int O0>
+__device__ __forceinline__ void lds_read_tr16(u32x2_t& a, uint32_t addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(a) : "v"(addr), "i"(O0) : "memory");
+}
+__device__ __forceinline__ void lds_wait_tr2(u32x2_t& a, u32x2_t& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b)::"memory");
+}
 // Wait for all outstanding LDS reads of this wave; the operands tie the results of
 // earlier lds_read_tr16x2 calls to this point, so no use of them moves above the wait.
 __device__ __forceinline__ void lds_wait_tr(u32x2_t& a, u32x2_t& b, u32x2_t& c, u32x2_t& d) {
