@@ -209,6 +209,10 @@ bwd_main_kernel(BwdParams p) {
   }
   const int per_head = (k0 < lk) ? (nqt > qt0 ? nqt - qt0 : 0) : 0;
   const int iters = per_head * p.G;
+  // Tile order: last query tile first, the group's heads innermost.  Every key tile of
+  // a KV head then visits the same (query tile, head) at about the same time, so Q, dO
+  // and the dQ accumulator rows of that tile are shared in L2 instead of being fetched
+  // once per key tile.
 
   // one query tile `it` (head gi, tile qt) into ring slot `slot`; past the last tile
   // the descriptors are empty and the slot is filled with zeros
@@ -216,8 +220,8 @@ bwd_main_kernel(BwdParams p) {
     unsigned char* dst = ring + slot * T::SLOT;
     int gi = 0, q0 = 0, rows = 0;
     if (it < iters) {
-      gi = it / per_head;
-      q0 = (qt0 + it % per_head) * BR;
+      gi = it % p.G;
+      q0 = (nqt - 1 - it / p.G) * BR;
       rows = p.Nq - q0;
     }
     const int hq = hkv * p.G + gi;
@@ -254,7 +258,7 @@ bwd_main_kernel(BwdParams p) {
   for (int it = 0; it < iters; ++it) {
     const int slot = it % NS;
     issue(it + 2, (it + 2) % NS);
-    const int gi = it / per_head, qt = qt0 + it % per_head;
+    const int gi = it % p.G, qt = nqt - 1 - it / p.G;
     const int hq = hkv * p.G + gi;
     const int q0 = qt * BR;
     const unsigned char* qs = ring + slot * T::SLOT;
@@ -326,51 +330,73 @@ bwd_main_kernel(BwdParams p) {
     // (4) dV += P^T dO and dK += dS^T Q; k-step ts = 2 qb + h2 holds queries
     //     16 ts + 8 (e/4) + 4 hi + e%4, which the transposing reads of dO and Q reproduce
 #pragma unroll
-    for (int d = 0; d < T::DB; ++d) {
-      u32x2_t o[4][2], q[4][2];
+    for (int d0 = 0; d0 < T::DB; d0 += 2) {
+      u32x2_t o[2][4][2], q[2][4][2];
 #pragma unroll
-      for (int ts = 0; ts < 4; ++ts)
+      for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int row = 16 * ts + 8 * r + vrow;
-          const uint32_t off = ring_addr + slot * T::SLOT + 16 * ts * T::ROWB +
-                               tr_off(T::ROWB, r, d, T::swz(row));
-          lds_read_tr16x2<0, T::QBYTES>(q[ts][r], o[ts][r], off);
-        }
-      lds_wait_tr(o[0][0], o[0][1], o[1][0], o[1][1]);
-      lds_wait_tr(o[2][0], o[2][1], o[3][0], o[3][1]);
-      lds_wait_tr(q[0][0], q[0][1], q[1][0], q[1][1]);
-      lds_wait_tr(q[2][0], q[2][1], q[3][0], q[3][1]);
+        for (int ts = 0; ts < 4; ++ts)
 #pragma unroll
-      for (int ts = 0; ts < 4; ++ts) {
-        dv[d] = mfma32(pa[ts >> 1][ts & 1], u32x4_t{o[ts][0][0], o[ts][0][1], o[ts][1][0], o[ts][1][1]}, dv[d]);
-        dk[d] = mfma32(da[ts >> 1][ts & 1], u32x4_t{q[ts][0][0], q[ts][0][1], q[ts][1][0], q[ts][1][1]}, dk[d]);
+          for (int r = 0; r < 2; ++r) {
+            const int row = 16 * ts + 8 * r + vrow;
+            const uint32_t off = ring_addr + slot * T::SLOT + 16 * ts * T::ROWB +
+                                 tr_off(T::ROWB, r, d0 + dd, T::swz(row));
+            lds_read_tr16x2<0, T::QBYTES>(q[dd][ts][r], o[dd][ts][r], off);
+          }
+#pragma unroll
+      for (int dd = 0; dd < 2; ++dd) {
+        lds_wait_tr(o[dd][0][0], o[dd][0][1], o[dd][1][0], o[dd][1][1]);
+        lds_wait_tr(o[dd][2][0], o[dd][2][1], o[dd][3][0], o[dd][3][1]);
+        lds_wait_tr(q[dd][0][0], q[dd][0][1], q[dd][1][0], q[dd][1][1]);
+        lds_wait_tr(q[dd][2][0], q[dd][2][1], q[dd][3][0], q[dd][3][1]);
       }
+#pragma unroll
+      for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+        for (int ts = 0; ts < 4; ++ts) {
+          const int d = d0 + dd;
+          dv[d] = mfma32(pa[ts >> 1][ts & 1],
+                         u32x4_t{o[dd][ts][0][0], o[dd][ts][0][1], o[dd][ts][1][0], o[dd][ts][1][1]}, dv[d]);
+          dk[d] = mfma32(da[ts >> 1][ts & 1],
+                         u32x4_t{q[dd][ts][0][0], q[dd][ts][0][1], q[dd][ts][1][0], q[dd][ts][1][1]}, dk[d]);
+        }
     }
 
     wait_ring();         // tile it + 1 has landed (only tile it + 2 may be in flight)
     FA_WAIT_LGKMCNT0();  // this wave's dS^T rows are written, its ring reads done
     FA_BARRIER();
 
-    // (5) dQ[:, 32 dsl ..) += dS K over the tile's 128 keys, for this wave's row blocks
+    // (5) dQ[:, 32 dsl ..) += dS K over the tile's 128 keys, for this wave's row blocks;
+    //     every transposing read of dS is issued before the first wait
+    {
+      u32x2_t lo[QBW][BC / 16], up[QBW][BC / 16];
+      const uint32_t base = ds_addr + (it & 1) * T::DSBYTES;
 #pragma unroll
-    for (int qq = 0; qq < QBW; ++qq) {
-      const int qb = qb0 + qq;
-      f32x16_t dq = f32x16_t{};
+      for (int qq = 0; qq < QBW; ++qq)
 #pragma unroll
-      for (int ks = 0; ks < BC / 16; ++ks) {
-        u32x2_t lo, up;
-        const uint32_t base = ds_addr + (it & 1) * T::DSBYTES + 16 * ks * T::DS_ROWB;
-        lds_read_tr16<0>(lo, base + tr_off(T::DS_ROWB, 0, qb, swz_ds(16 * ks + vrow)));
-        lds_read_tr16<0>(up, base + tr_off(T::DS_ROWB, 1, qb, swz_ds(16 * ks + 8 + vrow)));
-        lds_wait_tr2(lo, up);
-        dq = mfma32(u32x4_t{lo[0], lo[1], up[0], up[1]}, ktf[ks], dq);
-      }
-      float* dqa = p.dq_acc + (((int64_t)b * p.Hq + hq) * p.Nq + q0 + 32 * qb) * D + 32 * dsl + l32;
+        for (int ks = 0; ks < BC / 16; ++ks) {
+          const uint32_t bk = base + 16 * ks * T::DS_ROWB;
+          lds_read_tr16<0>(lo[qq][ks], bk + tr_off(T::DS_ROWB, 0, qb0 + qq, swz_ds(16 * ks + vrow)));
+          lds_read_tr16<0>(up[qq][ks], bk + tr_off(T::DS_ROWB, 1, qb0 + qq, swz_ds(16 * ks + 8 + vrow)));
+        }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (q0 + 32 * qb + ql < p.Nq) unsafeAtomicAdd(dqa + (int64_t)ql * D, dq[r]);
+      for (int qq = 0; qq < QBW; ++qq)
+#pragma unroll
+        for (int ks = 0; ks < BC / 16; ks += 2)
+          lds_wait_tr(lo[qq][ks], up[qq][ks], lo[qq][ks + 1], up[qq][ks + 1]);
+#pragma unroll
+      for (int qq = 0; qq < QBW; ++qq) {
+        const int qb = qb0 + qq;
+        f32x16_t dq = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < BC / 16; ++ks)
+          dq = mfma32(u32x4_t{lo[qq][ks][0], lo[qq][ks][1], up[qq][ks][0], up[qq][ks][1]}, ktf[ks], dq);
+        float* dqa = p.dq_acc + (((int64_t)b * p.Hq + hq) * p.Nq + q0 + 32 * qb) * D + 32 * dsl + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (q0 + 32 * qb + ql < p.Nq) unsafeAtomicAdd(dqa + (int64_t)ql * D, dq[r]);
+        }
       }
     }
   }
