@@ -119,10 +119,10 @@ fa_status fa_fwd(const fa_fwd_args *args, void *stream);
  *   kv_lens, scale, causal as in the forward; rows of dk/dv at positions >= Lk are 0.
  * The workspace (device, caller-owned, at least fa_bwd_workspace_bytes() bytes, any
  * contents) holds, per query row, the pair (LSE * log2 e, D_i = rowsum(dO * O)) in
- * fp32 [B, Hq, Nq, 2] and the fp32 dQ accumulator [B, Hq, Nq, D]; it is initialised
- * by the call itself.  Three kernels run in stream
- * order: D_i (and accumulator clear), the dK/dV tile kernel with fp32 dQ atomics, and
- * the dQ conversion.  dQ is not bitwise reproducible run to run (atomic order).
+ * fp32 [B, Hq, Nq, 2]; it is written by the call itself.  Three kernels run in stream
+ * order: the per-row statistics, dK/dV (one workgroup per key tile) and dQ (one
+ * workgroup per query tile, recomputing S and dP).  No atomics are used: results are
+ * bitwise reproducible run to run.
  * ------------------------------------------------------------------------------- */
 typedef struct fa_bwd_args {
   const void *q, *k, *v, *o, *dout;

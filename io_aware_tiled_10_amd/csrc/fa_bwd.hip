@@ -8,22 +8,27 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = rowsum(dO * O),  dS = P * (dP - D_i),
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// gfx950 mapping (three kernels in stream order):
+// gfx950 mapping (three kernels in stream order, no atomics: every output element is
+// written once, so the backward is deterministic):
 //  1. bwd_pre: per query row, D_i = rowsum(dO * O) in fp32 and LSE * log2(e), stored
-//     side by side; the fp32 dQ accumulator row is cleared;
-//  2. bwd_main: one workgroup (4 waves) per 128-key tile of a KV head.  Each wave keeps
-//     its 32 keys' K and V rows (operands of S and dP), a 32-column slice of K^T (the
-//     operand of dQ) and the fp32 dK, dV accumulators in registers, and walks the
-//     64-row query tiles of every query head of the GQA group that can see the tile
-//     (causal: from the diagonal down).  Q, dO and the row statistics of each tile
-//     stream from L2/HBM straight into a three-slot LDS ring (LDS DMA, XOR-swizzled
-//     16-byte slots), two tiles ahead.  Per tile: S = Q K^T and dP = dO V^T on
-//     32x32x16 bf16 MFMA (one lane per key, so P and dS are already the A operands
-//     of dV += P^T dO and dK += dS^T Q), with dO^T and Q^T from transposing LDS
-//     reads; dS^T goes to LDS with 8-byte writes, and after one barrier each wave
-//     reads dS back transposed to form its slice of dQ over the 128 keys, added into
-//     the fp32 accumulator with atomics;
-//  3. bwd_dq: dQ = scale * accumulator, rounded to bf16.
+//     side by side;
+//  2. bwd_kv: one workgroup (4 waves) per 128-key tile of a KV head.  Each wave keeps
+//     its 32 keys' K and V rows (operands of S and dP) and the fp32 dK, dV accumulators
+//     in registers, and walks the 64-row query tiles of every query head of the GQA
+//     group that can see the tile (causal: from the diagonal down).  Q, dO and the row
+//     statistics of each tile stream from L2/HBM straight into a three-slot LDS ring
+//     (LDS DMA, XOR-swizzled 16-byte slots), two tiles ahead.  Per tile: S = Q K^T and
+//     dP = dO V^T on 32x32x16 bf16 MFMA (one lane per key, so P and dS are already the
+//     A operands of dV += P^T dO and dK += dS^T Q), with dO^T and Q^T from transposing
+//     LDS reads;
+//  3. bwd_q: the forward's layout turned to dQ.  One workgroup (8 waves) per 256-row
+//     query tile, Q and dO rows resident as MFMA operands, K/V blocks of 64 keys
+//     through a three-slot LDS ring; per block S^T = K Q^T and dP^T = V dO^T (one lane
+//     per query), P^T = exp(S^T - LSE), dS^T = P^T (dP^T - D_i), and
+//     dQ^T += K^T dS^T with K^T from transposing reads; dQ = scale * acc, once.
+//     Recomputing S and dP here costs two more products per (query, key) pair than
+//     accumulating dQ inside bwd_kv, but removes the device-scope fp32 atomics, which
+//     on a multi-XCD part are executed beyond the per-XCD L2.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -32,9 +37,19 @@ namespace fa {
 namespace {
 
 constexpr int kBwdWaves = 4;
-constexpr int kBwdBC = 32 * kBwdWaves;  // keys per workgroup (32 per wave)
-constexpr int kBwdBR = 64;              // query rows per tile
-constexpr int kBwdSlots = 3;            // ring depth: Q, dO and statistics of one tile
+constexpr int kBwdBC = 32 * kBwdWaves;  // keys per bwd_kv workgroup (32 per wave)
+constexpr int kBwdBR = 64;              // query rows per bwd_kv tile
+constexpr int kBwdSlots = 3;            // ring depth
+
+// 16-byte slot swizzle of row r of a staged tile with `rowb`-byte rows: 16 consecutive
+// rows read at one logical slot hit 16 different slots, and 8 consecutive rows read over
+// an aligned group of 4 logical slots (transposing reads) cover every slot exactly twice.
+template <int ROWB>
+__device__ __forceinline__ int swz_rows(int r) {
+  constexpr int RPB = 256 / ROWB, SPR = ROWB / 16;
+  const int a = r / RPB;
+  return 4 * (a % (SPR / 4)) + (a / (SPR / 4)) % 4;
+}
 
 template <int D>
 struct BwdTile {
@@ -42,7 +57,6 @@ struct BwdTile {
   static constexpr int DB = D / 32;                       // 32-column blocks of the head dim
   static constexpr int ROWB = D * 2;                      // bytes per staged row
   static constexpr int SPR = D / 8;                       // 16-byte slots per row
-  static constexpr int RPB = 256 / ROWB;                  // rows per 256-byte bank period
   static constexpr int RPI = 1024 / ROWB;                 // rows per wave DMA instruction
   static constexpr int QBYTES = kBwdBR * ROWB;            // one Q or dO tile
   static constexpr int NDMA = QBYTES / (1024 * kBwdWaves);  // per thread per tensor
@@ -51,26 +65,13 @@ struct BwdTile {
   static constexpr int SLOT = 2 * QBYTES + 1024;          // Q, dO, 64 x (lse2, D_i) + pad
   static constexpr int RING = kBwdSlots * SLOT;
   static constexpr int KVBYTES = 2 * kBwdBC * ROWB;       // K and V tiles (set-up only)
-  static constexpr int DS_ROWB = kBwdBR * 2;              // dS^T row: 64 queries, bf16
-  static constexpr int DSBYTES = kBwdBC * DS_ROWB;        // one dS^T buffer
-  static constexpr int DSOFF = RING > KVBYTES ? RING : KVBYTES;
-  static constexpr int LDS_BYTES = DSOFF + 2 * DSBYTES;
-  static constexpr int NSL = DB;                          // 32-wide dQ column slices
-  static constexpr int QBW = 2 * NSL / kBwdWaves;         // 32-row dQ blocks per wave
+  static constexpr int LDS_BYTES = RING > KVBYTES ? RING : KVBYTES;
   static_assert(NDMA * 1024 * kBwdWaves == QBYTES, "a tile must split evenly over the waves");
-  // 16-byte slot swizzle of staged row r: 16 consecutive rows read at one logical slot
-  // hit 16 different slots, and 8 consecutive rows read over an aligned group of 4
-  // logical slots (transposing reads) cover every slot exactly twice
-  static __device__ __forceinline__ int swz(int r) {
-    const int a = r / RPB;
-    return 4 * (a % (SPR / 4)) + (a / (SPR / 4)) % 4;
-  }
+  static __device__ __forceinline__ int swz(int r) { return swz_rows<ROWB>(r); }
 };
-// dS^T rows are 128 bytes: the geometry of a D = 64 tile
-__device__ __forceinline__ int swz_ds(int r) { return BwdTile<64>::swz(r); }
 
-// Per query row: stats = (LSE * log2 e, D_i = sum_d dO_id O_id); zero the dQ accumulator
-// row.  Rows whose LSE is -inf (no visible key) get +inf, so their P is exactly zero.
+// Per query row: stats = (LSE * log2 e, D_i = sum_d dO_id O_id).  Rows whose LSE is -inf
+// (no visible key) get +inf, so their P is exactly zero.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
   constexpr int TPR = D / 8;            // threads per row
@@ -88,9 +89,6 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
     const u32x4_t g = *reinterpret_cast<const u32x4_t*>(p.dout + b * p.dos0 + hq * p.dos1 + (int64_t)i * p.dos2 + col);
 #pragma unroll
     for (int w = 0; w < 4; ++w) sum += bf16_lo(o[w]) * bf16_lo(g[w]) + bf16_hi(o[w]) * bf16_hi(g[w]);
-    float* acc = p.dq_acc + row * D + col;
-    *reinterpret_cast<f32x4_t*>(acc) = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4_t*>(acc + 4) = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, TPR);
@@ -104,12 +102,11 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
 
 template <int D>
 __global__ void __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
-bwd_main_kernel(BwdParams p) {
+bwd_kv_kernel(BwdParams p) {
   using T = BwdTile<D>;
   constexpr int BC = kBwdBC, BR = kBwdBR, NW = kBwdWaves, NS = kBwdSlots;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[T::LDS_BYTES];
   unsigned char* ring = lds;
-  unsigned char* dsbuf = lds + T::DSOFF;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -146,12 +143,11 @@ bwd_main_kernel(BwdParams p) {
   };
 
   // ---- set-up: K and V tiles into LDS, then the resident operands
-  const uint16_t* kbase = p.k + b * p.ks0 + hkv * p.ks1 + (int64_t)k0 * p.ks2;
-  const uint16_t* vbase = p.v + b * p.vs0 + hkv * p.vs1 + (int64_t)k0 * p.vs2;
   {
     const int valid = k0 < lk ? lk - k0 : 0;
-    dma_rows(kbase, p.ks2, BC, valid, ring, T::NDMA_KV);
-    dma_rows(vbase, p.vs2, BC, valid, ring + BC * T::ROWB, T::NDMA_KV);
+    dma_rows(p.k + b * p.ks0 + hkv * p.ks1 + (int64_t)k0 * p.ks2, p.ks2, BC, valid, ring, T::NDMA_KV);
+    dma_rows(p.v + b * p.vs0 + hkv * p.vs1 + (int64_t)k0 * p.vs2, p.vs2, BC, valid,
+             ring + BC * T::ROWB, T::NDMA_KV);
     FA_WAIT_VMCNT(0);
     __syncthreads();
   }
@@ -166,9 +162,11 @@ bwd_main_kernel(BwdParams p) {
       vf[ks] = *reinterpret_cast<const u32x4_t*>(ring + BC * T::ROWB + o);
     }
   }
+  FA_WAIT_LGKMCNT0();
+  __syncthreads();  // the ring reuses the K/V staging area
+
   // Transposing-read geometry (lane 16 g + i reads row 16 ts + 8 r + 4 (g/2) + i/4 and 4
-  // columns from 32 blk + 16 (g%2) + 4 (i%4)).  For any tile row period the swizzle of
-  // that row is 4 X + (2 r + g/2) % 4 with X depending on the lane only.
+  // columns from 32 blk + 16 (g%2) + 4 (i%4)).
   const int vg = lane >> 4, vi = lane & 15;
   const int vrow = 4 * (vg >> 1) + (vi >> 2);
   const int vlo = 2 * (vg & 1) + ((vi & 3) >> 1);
@@ -176,26 +174,6 @@ bwd_main_kernel(BwdParams p) {
     const int row = 8 * r + vrow;
     return row * rowb + 16 * ((4 * blk + vlo) ^ swz_row) + 8 * (vi & 1);
   };
-  // K^T slice of this wave's dQ columns: B operand of dQ = dS K, keys in the order the
-  // transposing reads of dS^T produce
-  constexpr int QBW = T::QBW;                 // dQ row blocks of this wave
-  const int dsl = wave % T::NSL;              // its 32-column slice of the head dim
-  const int qb0 = (wave / T::NSL) * QBW;      // its first 32-row dQ block
-  u32x4_t ktf[BC / 16];
-#pragma unroll
-  for (int ks = 0; ks < BC / 16; ++ks) {
-    u32x2_t lo, up;
-    const int r0 = 16 * ks + vrow, r1 = 16 * ks + 8 + vrow;
-    const uint32_t a = lds_addr(ring);
-    const uint32_t o0 = a + 16 * ks * T::ROWB + tr_off(T::ROWB, 0, dsl, T::swz(r0));
-    const uint32_t o1 = a + 16 * ks * T::ROWB + tr_off(T::ROWB, 1, dsl, T::swz(r1));
-    lds_read_tr16<0>(lo, o0);
-    lds_read_tr16<0>(up, o1);
-    lds_wait_tr2(lo, up);
-    ktf[ks] = u32x4_t{lo[0], lo[1], up[0], up[1]};
-  }
-  FA_WAIT_LGKMCNT0();
-  __syncthreads();  // the ring reuses the K/V staging area
 
   f32x16_t dk[T::DB], dv[T::DB];
 #pragma unroll
@@ -210,12 +188,11 @@ bwd_main_kernel(BwdParams p) {
   const int per_head = (k0 < lk) ? (nqt > qt0 ? nqt - qt0 : 0) : 0;
   const int iters = per_head * p.G;
   // Tile order: last query tile first, the group's heads innermost.  Every key tile of
-  // a KV head then visits the same (query tile, head) at about the same time, so Q, dO
-  // and the dQ accumulator rows of that tile are shared in L2 instead of being fetched
-  // once per key tile.
+  // a KV head then visits the same (query tile, head) at about the same time, so the
+  // tile's Q and dO rows are shared in L2.
 
-  // one query tile `it` (head gi, tile qt) into ring slot `slot`; past the last tile
-  // the descriptors are empty and the slot is filled with zeros
+  // one query tile `it` into ring slot `slot`; past the last tile the descriptors are
+  // empty and the slot is filled with zeros
   auto issue = [&](int it, int slot) {
     unsigned char* dst = ring + slot * T::SLOT;
     int gi = 0, q0 = 0, rows = 0;
@@ -245,7 +222,7 @@ bwd_main_kernel(BwdParams p) {
   static_assert(T::NDMA == 4 || T::NDMA == 2, "ring waits assume D = 128 or 64");
 
   const int qsw = T::swz(l32);  // plain reads of query rows 32 qb + l32
-  const uint32_t ring_addr = lds_addr(ring), ds_addr = lds_addr(dsbuf);
+  const uint32_t ring_addr = lds_addr(ring);
   const float c = p.scale_log2;
 
   if (iters > 0) {
@@ -258,8 +235,7 @@ bwd_main_kernel(BwdParams p) {
   for (int it = 0; it < iters; ++it) {
     const int slot = it % NS;
     issue(it + 2, (it + 2) % NS);
-    const int gi = it % p.G, qt = nqt - 1 - it / p.G;
-    const int hq = hkv * p.G + gi;
+    const int qt = nqt - 1 - it / p.G;
     const int q0 = qt * BR;
     const unsigned char* qs = ring + slot * T::SLOT;
     const unsigned char* dos = qs + T::QBYTES;
@@ -315,19 +291,7 @@ bwd_main_kernel(BwdParams p) {
           da[qb][h2][w] = pack_bf16(dp[qb][8 * h2 + 2 * w], dp[qb][8 * h2 + 2 * w + 1]);
         }
 
-    // (3) dS^T into LDS (double buffered): row = key, 4 consecutive queries per write
-    {
-      unsigned char* dsw = dsbuf + (it & 1) * T::DSBYTES + kwl * T::DS_ROWB + 8 * hi;
-      const int sw = swz_ds(kwl);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          *reinterpret_cast<u32x2_t*>(dsw + 16 * ((4 * qb + a) ^ sw)) =
-              u32x2_t{da[qb][a >> 1][2 * (a & 1)], da[qb][a >> 1][2 * (a & 1) + 1]};
-    }
-
-    // (4) dV += P^T dO and dK += dS^T Q; k-step ts = 2 qb + h2 holds queries
+    // (3) dV += P^T dO and dK += dS^T Q; k-step ts = 2 qb + h2 holds queries
     //     16 ts + 8 (e/4) + 4 hi + e%4, which the transposing reads of dO and Q reproduce
 #pragma unroll
     for (int d0 = 0; d0 < T::DB; d0 += 2) {
@@ -363,42 +327,8 @@ bwd_main_kernel(BwdParams p) {
     }
 
     wait_ring();         // tile it + 1 has landed (only tile it + 2 may be in flight)
-    FA_WAIT_LGKMCNT0();  // this wave's dS^T rows are written, its ring reads done
+    FA_WAIT_LGKMCNT0();  // this wave's ring reads are done
     FA_BARRIER();
-
-    // (5) dQ[:, 32 dsl ..) += dS K over the tile's 128 keys, for this wave's row blocks;
-    //     every transposing read of dS is issued before the first wait
-    {
-      u32x2_t lo[QBW][BC / 16], up[QBW][BC / 16];
-      const uint32_t base = ds_addr + (it & 1) * T::DSBYTES;
-#pragma unroll
-      for (int qq = 0; qq < QBW; ++qq)
-#pragma unroll
-        for (int ks = 0; ks < BC / 16; ++ks) {
-          const uint32_t bk = base + 16 * ks * T::DS_ROWB;
-          lds_read_tr16<0>(lo[qq][ks], bk + tr_off(T::DS_ROWB, 0, qb0 + qq, swz_ds(16 * ks + vrow)));
-          lds_read_tr16<0>(up[qq][ks], bk + tr_off(T::DS_ROWB, 1, qb0 + qq, swz_ds(16 * ks + 8 + vrow)));
-        }
-#pragma unroll
-      for (int qq = 0; qq < QBW; ++qq)
-#pragma unroll
-        for (int ks = 0; ks < BC / 16; ks += 2)
-          lds_wait_tr(lo[qq][ks], up[qq][ks], lo[qq][ks + 1], up[qq][ks + 1]);
-#pragma unroll
-      for (int qq = 0; qq < QBW; ++qq) {
-        const int qb = qb0 + qq;
-        f32x16_t dq = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < BC / 16; ++ks)
-          dq = mfma32(u32x4_t{lo[qq][ks][0], lo[qq][ks][1], up[qq][ks][0], up[qq][ks][1]}, ktf[ks], dq);
-        float* dqa = p.dq_acc + (((int64_t)b * p.Hq + hq) * p.Nq + q0 + 32 * qb) * D + 32 * dsl + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (q0 + 32 * qb + ql < p.Nq) unsafeAtomicAdd(dqa + (int64_t)ql * D, dq[r]);
-        }
-      }
-    }
   }
 
   // ---- dK = scale * acc, dV = acc, rounded to bf16; rows >= Nk are not stored (rows in
@@ -425,24 +355,226 @@ bwd_main_kernel(BwdParams p) {
     }
 }
 
-// dQ = scale * accumulator -> bf16, eight elements per thread.
+// ------------------------------------------------------------------------------------
+// dQ: query-tile outer loop, the forward's layout (one lane per query, K/V streamed).
+// ------------------------------------------------------------------------------------
+constexpr int kDqWaves = 8;
+constexpr int kDqBR = 32 * kDqWaves;  // query rows per workgroup
+constexpr int kDqBC = 64;             // keys per block
+constexpr int kDqSlots = 3;
+
 template <int D>
-__global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
-  constexpr int TPR = D / 8;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = idx / TPR;
-  if (row >= (int64_t)p.B * p.Hq * p.Nq) return;
-  const int col = 8 * (int)(idx % TPR);
-  const int i = (int)(row % p.Nq);
-  const int64_t bh = row / p.Nq;
-  const int hq = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-  const float* a = p.dq_acc + row * D + col;
-  const f32x4_t x = *reinterpret_cast<const f32x4_t*>(a);
-  const f32x4_t y = *reinterpret_cast<const f32x4_t*>(a + 4);
-  const float sc = p.scale;
-  *reinterpret_cast<u32x4_t*>(p.dq + b * p.dqs0 + hq * p.dqs1 + (int64_t)i * p.dqs2 + col) =
-      u32x4_t{pack_bf16(x[0] * sc, x[1] * sc), pack_bf16(x[2] * sc, x[3] * sc),
-              pack_bf16(y[0] * sc, y[1] * sc), pack_bf16(y[2] * sc, y[3] * sc)};
+struct DqTile {
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int ROWB = D * 2;
+  static constexpr int SPR = D / 8;
+  static constexpr int RPI = 1024 / ROWB;
+  static constexpr int TBYTES = kDqBC * ROWB;                // one K or V block
+  static constexpr int NDMA = TBYTES / (1024 * kDqWaves);    // per thread per tensor
+  static constexpr int LDS_BYTES = 2 * kDqSlots * TBYTES;
+  static_assert(NDMA * 1024 * kDqWaves == TBYTES, "a block must split evenly over the waves");
+  static __device__ __forceinline__ int swz(int r) { return swz_rows<ROWB>(r); }
+};
+
+template <int D>
+__global__ void __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_q_kernel(BwdParams p) {
+  using T = DqTile<D>;
+  constexpr int BR = kDqBR, BC = kDqBC, NW = kDqWaves, NS = kDqSlots;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[T::LDS_BYTES];
+  unsigned char* kring = lds;
+  unsigned char* vring = lds + NS * T::TBYTES;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  // tile: XCD-contiguous, KV-head-major, heavy causal tiles first (as the forward)
+  int t = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int gi = t % p.G;
+  t /= p.G;
+  const int nqt = (p.Nq + BR - 1) / BR;
+  const int rank = t % nqt;
+  t /= nqt;
+  const int hkv = t % p.Hkv;
+  const int b = t / p.Hkv;
+  const int qt = p.causal ? nqt - 1 - rank : rank;
+  const int hq = hkv * p.G + gi;
+
+  int lk = p.Nk;
+  if (p.kv_lens) {
+    lk = p.kv_lens[b];
+    lk = lk < 0 ? 0 : (lk > p.Nk ? p.Nk : lk);
+  }
+  const int diag = lk - p.Nq;
+  const int q_wg0 = qt * BR;
+  int kend = lk;
+  if (p.causal) {
+    const int lim = q_wg0 + BR + diag;
+    kend = lim < kend ? lim : kend;
+  }
+  if (kend < 0) kend = 0;
+  const int nblk = (kend + BC - 1) / BC;
+  const int qi = q_wg0 + wave * 32 + l32;  // this lane's query row
+
+  uint16_t* dqrow = p.dq + b * p.dqs0 + hq * p.dqs1 + (int64_t)qi * p.dqs2;
+  if (nblk == 0) {  // no visible key: dQ = 0
+    if (qi < p.Nq)
+      for (int d = 4 * hi; d < D; d += 8) *reinterpret_cast<u32x2_t*>(dqrow + d) = u32x2_t{};
+    return;  // uniform over the workgroup
+  }
+
+  // Q and dO rows of this lane's query as B operands (k-elements = head dim), and its
+  // (LSE log2 e, D_i); rows past Nq read as zero
+  u32x4_t qf[T::KS], df[T::KS];
+  float l2 = 0.f, dd = 0.f;
+  {
+    const int rows = min(BR, p.Nq - q_wg0);
+    const auto rq = make_rsrc(p.q + b * p.qs0 + hq * p.qs1 + (int64_t)q_wg0 * p.qs2,
+                              rows_span(rows, p.qs2 * 2, D * 2));
+    const auto rd = make_rsrc(p.dout + b * p.dos0 + hq * p.dos1 + (int64_t)q_wg0 * p.dos2,
+                              rows_span(rows, p.dos2 * 2, D * 2));
+    const uint32_t oq = (uint32_t)((wave * 32 + l32) * p.qs2 * 2) + 16 * hi;
+    const uint32_t od = (uint32_t)((wave * 32 + l32) * p.dos2 * 2) + 16 * hi;
+#pragma unroll
+    for (int s = 0; s < T::KS; ++s) {
+      qf[s] = buf_load16(rq, oq + 32 * s);
+      df[s] = buf_load16(rd, od + 32 * s);
+    }
+    if (qi < p.Nq) {
+      typedef float f32x2_t __attribute__((ext_vector_type(2)));
+      const f32x2_t st = reinterpret_cast<const f32x2_t*>(p.stats)[((int64_t)b * p.Hq + hq) * p.Nq + qi];
+      l2 = st[0];
+      dd = st[1];
+    } else {
+      l2 = INFINITY;  // padding rows: P = 0
+    }
+    asm volatile("" ::: "memory");  // issue these before the ring loads below
+  }
+
+  const uint16_t* kbase = p.k + b * p.ks0 + hkv * p.ks1;
+  const uint16_t* vbase = p.v + b * p.vs0 + hkv * p.vs1;
+  const int64_t kpitch = p.ks2 * 2, vpitch = p.vs2 * 2;
+  const int drow = T::RPI * wave + lane / T::SPR, dslot = lane % T::SPR;
+  const int dswz = dslot ^ T::swz(drow);
+  const uint32_t kdma = (uint32_t)(drow * kpitch) + 16 * dswz;
+  const uint32_t vdma = (uint32_t)(drow * vpitch) + 16 * dswz;
+  const int kstep = (int)(NW * T::RPI * kpitch), vstep = (int)(NW * T::RPI * vpitch);
+  auto dma = [&](int blk, int slot) {  // blocks past the keys fill the slot with zeros
+    const int key0 = blk * BC;
+    const auto rk = make_rsrc(kbase + (int64_t)key0 * p.ks2, rows_span(min(BC, lk - key0), kpitch, D * 2));
+    const auto rv = make_rsrc(vbase + (int64_t)key0 * p.vs2, rows_span(min(BC, lk - key0), vpitch, D * 2));
+#pragma unroll
+    for (int i = 0; i < T::NDMA; ++i)
+      lds_dma16(rk, kring + slot * T::TBYTES + 1024 * (NW * i + wave), kdma, 0, kstep * i);
+#pragma unroll
+    for (int i = 0; i < T::NDMA; ++i)
+      lds_dma16(rv, vring + slot * T::TBYTES + 1024 * (NW * i + wave), vdma, 0, vstep * i);
+  };
+
+  // transposing-read geometry for K^T (rows = keys 16 ts + 8 r + 4 (g/2) + i/4)
+  const int vg = lane >> 4, vi = lane & 15;
+  const int vrow = 4 * (vg >> 1) + (vi >> 2);
+  const int vlo = 2 * (vg & 1) + ((vi & 3) >> 1);
+  const int rsw = T::swz(l32);  // plain reads of key rows l32 and 32 + l32
+  const uint32_t kring_addr = lds_addr(kring);
+
+  f32x16_t acc[T::DB];
+#pragma unroll
+  for (int d = 0; d < T::DB; ++d) acc[d] = f32x16_t{};
+  const float c = p.scale_log2;
+
+  dma(0, 0);
+  dma(1, 1);
+  if constexpr (T::NDMA == 2) FA_WAIT_VMCNT(4); else FA_WAIT_VMCNT(2);
+  FA_BARRIER();
+
+  for (int j = 0; j < nblk; ++j) {
+    const int slot = j % NS;
+    dma(j + 2, (j + 2) % NS);  // into the slot block j - 1 finished with
+    const unsigned char* ks = kring + slot * T::TBYTES;
+    const unsigned char* vs = vring + slot * T::TBYTES;
+
+    // S^T = K Q^T and dP^T = V dO^T for keys [0, 32) and [32, 64) of the block
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) s[h] = dp[h] = f32x16_t{};
+#pragma unroll
+    for (int k = 0; k < T::KS; ++k) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int o = (32 * h + l32) * T::ROWB + 16 * ((2 * k + hi) ^ rsw);
+        const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(ks + o);
+        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(vs + o);
+        s[h] = mfma32(ak, qf[k], s[h]);
+        dp[h] = mfma32(av, df[k], dp[h]);
+      }
+    }
+
+    // P^T = exp(S^T - LSE), dS^T = P^T (dP^T - D_i), zero where the pair does not exist;
+    // packed as the B operand of dQ^T += K^T dS^T (k-step ts: keys 16 ts + 8 (e/4) +
+    // 4 hi + e%4, e = 0..7)
+    const int key0 = j * BC;
+    const bool edge = (key0 + BC > lk) || (p.causal && key0 + BC - 1 > q_wg0 + diag);
+    const int last = p.causal ? min(lk - 1, qi + diag) : lk - 1;
+    u32x4_t pf[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float v2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float pv = fast_exp2(fmaf(s[h][r + e], c, -l2));
+          float ds = pv * (dp[h][r + e] - dd);
+          if (edge) {
+            const int key = key0 + 32 * h + 8 * ((r + e) >> 2) + 4 * hi + ((r + e) & 3);
+            ds = key > last ? 0.f : ds;
+          }
+          v2[e] = ds;
+        }
+        pf[2 * h + (r >> 3)][(r & 7) >> 1] = pack_bf16(v2[0], v2[1]);
+      }
+
+    // dQ^T += K^T dS^T; K^T fragments from transposing reads of the K block
+#pragma unroll
+    for (int d = 0; d < T::DB; ++d) {
+      u32x2_t kt[4][2];
+#pragma unroll
+      for (int ts = 0; ts < 4; ++ts)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int row = 16 * ts + 8 * r + vrow;
+          const uint32_t off = kring_addr + slot * T::TBYTES + row * T::ROWB +
+                               16 * ((4 * d + vlo) ^ T::swz(row)) + 8 * (vi & 1);
+          lds_read_tr16<0>(kt[ts][r], off);
+        }
+      lds_wait_tr(kt[0][0], kt[0][1], kt[1][0], kt[1][1]);
+      lds_wait_tr(kt[2][0], kt[2][1], kt[3][0], kt[3][1]);
+#pragma unroll
+      for (int ts = 0; ts < 4; ++ts)
+        acc[d] = mfma32(u32x4_t{kt[ts][0][0], kt[ts][0][1], kt[ts][1][0], kt[ts][1][1]}, pf[ts], acc[d]);
+    }
+
+    // block j + 1 has landed (only block j + 2 may be in flight); the barrier publishes
+    // it and frees this block's slot
+    if constexpr (T::NDMA == 2) FA_WAIT_VMCNT(4); else FA_WAIT_VMCNT(2);
+    FA_WAIT_LGKMCNT0();
+    FA_BARRIER();
+  }
+
+  // ---- dQ = scale * acc (lane = query row, register = head-dim element)
+  if (qi < p.Nq) {
+    const float sc = p.scale;
+#pragma unroll
+    for (int d = 0; d < T::DB; ++d)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        *reinterpret_cast<u32x2_t*>(dqrow + 32 * d + 8 * rg + 4 * hi) =
+            u32x2_t{pack_bf16(acc[d][4 * rg] * sc, acc[d][4 * rg + 1] * sc),
+                    pack_bf16(acc[d][4 * rg + 2] * sc, acc[d][4 * rg + 3] * sc)};
+  }
 }
 
 template <typename K>
@@ -462,24 +594,22 @@ hipError_t launch_all(BwdParams p, hipStream_t stream) {
   hipError_t e = launch(bwd_pre_kernel<D>, (rows + RPB - 1) / RPB, 256, p, stream);
   if (e != hipSuccess) return e;
   p.nkt = (p.Nk + kBwdBC - 1) / kBwdBC;
-  e = launch(bwd_main_kernel<D>, (int64_t)p.nkt * p.Hkv * p.B, 64 * kBwdWaves, p, stream);
+  e = launch(bwd_kv_kernel<D>, (int64_t)p.nkt * p.Hkv * p.B, 64 * kBwdWaves, p, stream);
   if (e != hipSuccess) return e;
-  return launch(bwd_dq_kernel<D>, (rows * (D / 8) + 255) / 256, 256, p, stream);
+  const int64_t nqt = (p.Nq + kDqBR - 1) / kDqBR;
+  return launch(bwd_q_kernel<D>, nqt * p.Hq * p.B, 64 * kDqWaves, p, stream);
 }
-
-size_t stats_bytes(int B, int Hq, int Nq) { return ((size_t)B * Hq * Nq * 8 + 255) & ~size_t(255); }
 
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int Hq, int Nq, int D) {
-  const size_t rows = (size_t)B * Hq * Nq;
-  return stats_bytes(B, Hq, Nq) + ((rows * D * 4 + 255) & ~size_t(255));
+  (void)D;
+  return ((size_t)B * Hq * Nq * 8 + 255) & ~size_t(255);
 }
 
 void bwd_bind_workspace(BwdParams& p, void* workspace, int D) {
   (void)D;
   p.stats = static_cast<float*>(workspace);
-  p.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + stats_bytes(p.B, p.Hq, p.Nq));
 }
 
 hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t stream) {

@@ -73,3 +73,16 @@ def test_bwd_full_size_c4_sampled_heads():
             e = rel_l2(to_host(g[b:b + 1, h:h + 1]), r)
             say(f"  b{b} h{h} {nm} rel-L2 {e:.3e}")
             assert e <= 2e-2, (b, h, nm, e)
+
+
+def test_bwd_is_deterministic():
+    # no atomics anywhere in the backward: two calls give identical bits
+    say("bwd determinism")
+    x = inputs.attention_inputs(1, 8, 2, 300, 300, 128, "bf16", seed=4, with_grad=True)
+    q, k, v, do = to_dev(x.q), to_dev(x.k), to_dev(x.v), to_dev(x.do)
+    o, lse = fa.fwd(q, k, v, causal=True)
+    a = fa.bwd(q, k, v, o, do, lse, causal=True)
+    b = fa.bwd(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    for x1, x2 in zip(a, b):
+        assert torch.equal(x1, x2)
