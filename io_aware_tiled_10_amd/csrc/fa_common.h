@@ -100,6 +100,20 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, u
 // compiler barrier for memory accesses.
 #define FA_WAIT_VMCNT(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
 #define FA_WAIT_LGKMCNT0() asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory")
+// FA_WAIT_VMCNT for a compile-time count (the counts the ring pipelines use).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N == 0 || N == 1 || N == 2 || N == 4 || N == 5 || N == 8 || N == 9 || N == 16,
+                "add the count here");
+  if constexpr (N == 0) FA_WAIT_VMCNT(0);
+  else if constexpr (N == 1) FA_WAIT_VMCNT(1);
+  else if constexpr (N == 2) FA_WAIT_VMCNT(2);
+  else if constexpr (N == 4) FA_WAIT_VMCNT(4);
+  else if constexpr (N == 5) FA_WAIT_VMCNT(5);
+  else if constexpr (N == 8) FA_WAIT_VMCNT(8);
+  else if constexpr (N == 9) FA_WAIT_VMCNT(9);
+  else FA_WAIT_VMCNT(16);
+}
 // Workgroup barrier without the memory fence __syncthreads() adds (which waits for every
 // outstanding load, ring prefetches included).  Callers order LDS themselves: each wave
 // waits for its own ring loads (FA_WAIT_VMCNT) and LDS reads (lgkmcnt) before it.
