@@ -1,15 +1,16 @@
 """Benchmark of the attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs fwd,bwd,decode]
-                    [--no-cpu-baseline] [--aux]
+                    [--no-cpu-baseline] [--aux] [--calib-copy]
+    python bench.py --write-traffic FETCH_CSV WRITE_CSV
 
 One step runs the whole path once, each leg on its own synthetic workload with
 inputs already resident in HBM:
 
   fwd     causal GQA forward, B1 Hq32 Hkv8 N16384 D128, bf16, LSE saved
-  bwd     causal recompute backward, B2 H16 N4096 D128, bf16 (D_i pre-pass, dK/dV
-          tile kernel with dQ atomics, dQ conversion); O and LSE come from fa_fwd
-          on the same inputs before timing
+  bwd     causal recompute backward, B2 H16 N4096 D128, bf16 (per-row statistics,
+          dK/dV key-tile kernel, dQ query-tile kernel; no atomics); O and LSE come
+          from fa_fwd on the same inputs before timing
   decode  split-KV decode, 64 sequences x 1 token, Hq32 Hkv8 D128, bf16 cache,
           lengths U[1024, 32768] (seed 0), chunks of 2048 + merge
 
@@ -19,7 +20,11 @@ backward (five products, one of them the recompute of S).  Decode bandwidth coun
 each valid cached K/V byte once plus q and O.
 
 Prints one JSON line.  The CPU baseline times the fp64 oracle forward on a bounded
-sample (whole query heads of the forward workload) on the host cores.
+sample (whole query heads of the forward workload) on the host cores.  `roofline`
+describes the forward kernel (the largest share of the step): achieved = credited
+FLOPs / mean HIP-event duration of its launch; `traffic` = HBM bytes per launch from
+the committed counter summary (FETCH_SIZE and WRITE_SIZE scaled by their readings
+for a plain copy), null once the kernel sources no longer match it.
 """
 
 from __future__ import annotations
@@ -53,8 +58,12 @@ DEC_CFG = dict(Bs=64, Hq=32, Hkv=8, D=128, lo=1024, hi=32768, split=2048, lmax=3
 AUX_CFGS = {"fwd_b4h16n2048_noncausal": dict(B=4, Hq=16, Hkv=16, N=2048, D=128, causal=False),
             "fwd_b4h16n2048_causal": dict(B=4, Hq=16, Hkv=16, N=2048, D=128, causal=True)}
 
-FWD_KERNEL_SRC = os.path.join(ROOT, "io_aware_tiled_10_amd", "csrc", "fa_fwd.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_b1h32kv8n16384d128_causal_traffic.json")
+CSRC = os.path.join(ROOT, "io_aware_tiled_10_amd", "csrc")
+# sources the forward kernel's machine code depends on
+FWD_KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("fa_fwd.hip", "fa_common.h", "fa_internal.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_b1h32kv8n16384d128_causal_hbm_traffic.md")
+FWD_GRID_THREADS = 1048576  # workgroups x threads of the timed forward launch (rocprofv3 Grid_Size)
+COPY_BYTES = 256 << 20      # the --calib-copy transfer
 
 
 def log(*a):
@@ -173,15 +182,70 @@ def cpu_baseline(budget_s: float = 12.0):
                       f"D128 causal workload ({done * per_head / 1e9:.1f} GFLOP credited, {el:.1f} s)"}
 
 
-def traffic_for(kernel_src: str, path: str):
-    """HBM bytes per launch from the committed counter summary, if it is current."""
-    if not os.path.exists(path):
+def sources_sha256(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def traffic_for(paths, summary: str):
+    """HBM bytes per launch from the committed counter summary, if the kernel is unchanged."""
+    if not os.path.exists(summary):
         return None
-    rec = json.load(open(path))
-    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-    if rec.get("kernel_sha256") != h:
+    fields = {}
+    for line in open(summary):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel sources sha256") != sources_sha256(paths):
         return None
-    return rec.get("bytes_per_launch")
+    return int(fields["HBM bytes per launch"])
+
+
+def write_traffic_summary(fetch_csv: str, write_csv: str, out: str) -> None:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; with --calib-copy) into the
+    committed summary.  Each counter is scaled by what it reads for the plain 256 MiB copy."""
+    import csv
+
+    def per_kernel(path, counter):
+        fwd, copy = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if "fwd_bf16_kernel<128, false>" in r["Kernel_Name"] and int(r["Grid_Size"]) == FWD_GRID_THREADS:
+                fwd.append(v)
+            if "copyBuffer" in r["Kernel_Name"] and v > 0.25 * COPY_BYTES / 1024:
+                copy.append(v)
+        if not fwd or not copy:
+            raise SystemExit(f"{path}: no forward or calibration-copy dispatch with {counter}")
+        return float(np.mean(fwd)), float(np.mean(copy))
+
+    f_fwd, f_copy = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_fwd, w_copy = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = COPY_BYTES / 1024 / f_copy, COPY_BYTES / 1024 / w_copy
+    total = int(round((f_fwd * f_scale + w_fwd * w_scale) * 1024))
+    algo = 337_641_472  # Q, K, V, O (bf16) and LSE (fp32) of the workload, read/written once
+    with open(out, "w") as fh:
+        fh.write("# HBM traffic of fwd_bf16_kernel<128>, B1 Hq32 Hkv8 N16384 D128 causal\n\n")
+        fh.write("Commands (MI355X, repository root; one counter per run):\n\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            fh.write(f"    rocprofv3 --pmc {c} --output-format csv -d gpurun_out/<dir> -o run -- "
+                     "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy\n")
+        fh.write("\nThe counters are scaled by their reading for the plain 256 MiB device copy that "
+                 "`--calib-copy` runs in the same process (a copy kernel reads and writes exactly "
+                 "268,435,456 bytes).\n\n")
+        fh.write(f"- FETCH_SIZE KiB per forward launch: {f_fwd:.1f}\n")
+        fh.write(f"- FETCH_SIZE KiB of the copy: {f_copy:.1f} (scale {f_scale:.4f})\n")
+        fh.write(f"- WRITE_SIZE KiB per forward launch: {w_fwd:.1f}\n")
+        fh.write(f"- WRITE_SIZE KiB of the copy: {w_copy:.1f} (scale {w_scale:.4f})\n")
+        fh.write(f"- HBM bytes per launch: {total}\n")
+        fh.write(f"- algorithmic bytes per launch: {algo} (ratio {total / algo:.2f})\n")
+        fh.write(f"- kernel sources sha256: `{sources_sha256(FWD_KERNEL_SRCS)}`\n")
+        fh.write("\nbench.py reports `roofline.traffic` from the HBM-bytes line only while the kernel "
+                 "sources hash to the value above.\n")
+    print(f"wrote {out}: {total} bytes per launch", file=sys.stderr)
 
 
 # ------------------------------------------------------------------------------------
@@ -196,7 +260,12 @@ def main():
     ap.add_argument("--aux", action="store_true", help="also time the B4 H16 N2048 forwards")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM-traffic summary from two rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic_summary(args.write_traffic[0], args.write_traffic[1], TRAFFIC_FILE)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the forward shards over heads with no exchange; see DESIGN.md)", file=sys.stderr)
@@ -277,7 +346,7 @@ def main():
             del leg
 
     if args.calib_copy:
-        src = torch.empty(128 << 20, dtype=torch.bfloat16, device=DEV).fill_(1.0)
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=DEV).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)  # reads 256 MiB, writes 256 MiB
@@ -291,7 +360,7 @@ def main():
         roofline = {"kernel": "fwd_bf16_kernel<128> (one launch per fa_fwd call)", "bound": "mfma",
                     "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic_for(FWD_KERNEL_SRC, TRAFFIC_FILE)}
+                    "traffic": traffic_for(FWD_KERNEL_SRCS, TRAFFIC_FILE)}
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
