@@ -182,6 +182,46 @@ def cpu_baseline(budget_s: float = 12.0):
                       f"D128 causal workload ({done * per_head / 1e9:.1f} GFLOP credited, {el:.1f} s)"}
 
 
+def ceilings():
+    """Achievable rates on this GPU for the same data statistics, for context: a library
+    bf16 GEMM (hipBLASLt via torch.matmul, 8192^3) on N(0,1) data and on all-ones data
+    (the sustained clock depends on the data), and a 2 GiB device-to-device copy."""
+    res = {}
+    n = 8192
+    g = torch.Generator(device=DEV).manual_seed(0)
+    for name, fill in (("random", None), ("ones", 1.0)):
+        a = torch.randn(n, n, device=DEV, generator=g).to(torch.bfloat16) if fill is None else \
+            torch.full((n, n), fill, dtype=torch.bfloat16, device=DEV)
+        b = torch.randn(n, n, device=DEV, generator=g).to(torch.bfloat16) if fill is None else a.clone()
+        c = torch.empty(n, n, dtype=torch.bfloat16, device=DEV)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        it = 40  # ~1 s of sustained MFMA work
+        for _ in range(it):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / it
+        res[f"gemm_bf16_8192_{name}_tflops"] = round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+        del a, b, c
+    x = torch.ones(1 << 30, dtype=torch.bfloat16, device=DEV)  # 2 GiB
+    y = torch.empty_like(x)
+    y.copy_(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    res["device_copy_2gib_read_plus_write_gbs"] = round(2 * x.numel() * 2 / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9, 1)
+    del x, y
+    return res
+
+
 def sources_sha256(paths) -> str:
     h = hashlib.sha256()
     for p in paths:
@@ -260,6 +300,8 @@ def main():
     ap.add_argument("--aux", action="store_true", help="also time the B4 H16 N2048 forwards")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also measure a library bf16 GEMM and a streaming read (context only)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM-traffic summary from two rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
@@ -361,6 +403,10 @@ def main():
                     "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                     "traffic": traffic_for(FWD_KERNEL_SRCS, TRAFFIC_FILE)}
+    ceil = None
+    if args.ceilings:
+        log("measuring library GEMM / streaming-read ceilings ...")
+        ceil = ceilings()
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
@@ -378,6 +424,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if ceil is not None:
+        line["ceilings"] = ceil
     print(json.dumps(line), flush=True)
 
 
