@@ -13,10 +13,12 @@
 //    principle: no reduction across waves).  A K/V block staged in LDS serves all 256
 //    rows, halving the L2 -> LDS traffic per FLOP against 128-row tiles;
 //  * K/V blocks of 64 keys go from L2/HBM straight into LDS (LDS DMA: coalesced 1 KiB
-//    per wave instruction, no staging registers) through three-slot rings, with the
+//    per wave instruction, no staging registers) through four-slot rings, with the
 //    16-byte slots of every row XOR-swizzled so that the operand reads are free of
 //    bank conflicts.  K runs one block ahead of V; each load has two blocks of compute
-//    to land, and one barrier per block orders the ring;
+//    to land, and one barrier per block orders the ring.  The block loop is unrolled
+//    over the four slots so that every LDS operand address is a per-lane register plus
+//    an immediate offset;
 //  * the scores are computed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMA, so each
 //    lane holds one query's scores: the row max / sum are lane-local plus a single
 //    exchange between the two wave halves;
@@ -26,7 +28,11 @@
 //  * the probabilities stay in registers as the B operand of O^T += V^T P^T; the V^T
 //    operand comes from transposing LDS reads (ds_read_b64_tr_b16) in the key order of
 //    the score registers, so no shuffle is needed between the two products;
-//  * exp is exp2 with scale*log2(e) folded into one fma per score;
+//  * exp is exp2 with scale*log2(e) folded into one fma per score.  The exponent
+//    reference is a running maximum that is moved lazily: a block's probabilities are
+//    first taken against the current reference, and only if some lane's block sum
+//    exceeds 2^8 (always on the first block) are the scores recomputed and the row
+//    maximum, the reference and the rescale done; the common path has no max at all;
 //  * causal: blocks above the diagonal are never visited, the mask is applied only
 //    on blocks that cross it, and the heaviest query tiles are launched first;
 //  * workgroups are ordered so tiles that share a KV head run on the same XCD.
@@ -40,7 +46,7 @@ namespace {
 constexpr int kFwdWaves = 8;
 constexpr int kFwdBR = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBC = 64;              // keys per block
-constexpr int kFwdSlots = 3;            // ring depth for K and for V
+constexpr int kFwdSlots = 4;            // ring depth for K and for V
 
 template <int D>
 struct FwdTile {
@@ -58,12 +64,19 @@ struct FwdTile {
   static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPB) % (SPR / 4)); }
 };
 
-// The running maximum used as the exponent reference is only moved when a block's
-// maximum exceeds it by more than this many powers of two (per-wave decision).  Until
-// then probabilities may exceed 1 by at most 2^kLazyRescale, which bf16 P and the fp32
-// sums absorb; the final O = acc / l and LSE = m*scale + ln(l) use the same reference,
-// so the result is unchanged while almost every accumulator rescale is skipped.
-constexpr float kLazyRescale = 8.f;
+// A ring slot known at compile time, so that LDS addresses of a slot are immediate
+// offsets from per-lane base registers.
+template <int N>
+struct Slot {
+  static constexpr int value = N;
+};
+
+// The exponent reference m (a running maximum of the scores seen so far) is moved
+// only when some lane's probability sum over one block exceeds this bound, so every
+// probability stays at most 2^8: bf16 P and the fp32 sums absorb that, while the row
+// maximum and almost every accumulator rescale are skipped.  The final O = acc / l and
+// LSE = m*scale + ln(l) use the same reference, so the result does not depend on it.
+constexpr float kMaxBlockSum = 256.f;
 
 template <int D, bool OUT_F32>
 __global__ void __launch_bounds__(64 * kFwdWaves) __attribute__((amdgpu_waves_per_eu(2)))
@@ -181,75 +194,94 @@ fwd_bf16_kernel(FwdParams p) {
   const int vrow = 4 * (vg >> 1) + (vi >> 2);
   const int vsw = T::swz_v(vrow) >> 2;
   const uint32_t vlane = vrow * T::ROWB + 16 * (2 * (vg & 1) + ((vi & 3) >> 1)) + 8 * (vi & 1);
-  const uint32_t vring_addr = lds_addr(vring);
+  uint32_t vaddr[T::DB];  // per 32-column block of V, slot 0
+#pragma unroll
+  for (int d = 0; d < T::DB; ++d) vaddr[d] = lds_addr(vring) + vlane + 64 * (d ^ vsw);
 
   f32x16_t acc[T::DB];
 #pragma unroll
   for (int d = 0; d < T::DB; ++d) acc[d] = f32x16_t{};
   float m = -INFINITY, l = 0.f;  // m: exponent reference (raw score units)
   const float c = p.scale_log2;
-  const float thresh = kLazyRescale / c;
 
   // One block: (s0, s1) hold the scores of block j (keys 64 j + [0, 32), + [32, 64));
   // the scores of block j + 1 are produced into (n0, n1).
-  auto step = [&](int j, f32x16_t& s0, f32x16_t& s1, f32x16_t& n0, f32x16_t& n1) {
-    // K_{j+3} and V_{j+2} into the slots blocks j and j - 1 finished with
-    dma_k(j + 3, j % NS);
-    dma_v(j + 2, (j + 2) % NS);
+  // `slot` is j % NS.
+  auto step = [&](int j, auto slot, f32x16_t& s0, f32x16_t& s1, f32x16_t& n0, f32x16_t& n1) {
+    constexpr int sl = decltype(slot)::value;
+    constexpr uint32_t vo = sl * T::TBYTES;
+    // K_{j+3} and V_{j+2} into the slots of K_{j-1} and V_{j-2}, which are free
+    dma_k(j + 3, (sl + 3) % NS);
+    dma_v(j + 2, (sl + 2) % NS);
 
     const int key0 = j * BC;
     const bool edge = (key0 + BC > lk) || (p.causal && key0 + BC - 1 > q_wg0 + diag);
-    if (edge) {
-      const int last = p.causal ? min(lk - 1, qi + diag) : lk - 1;  // last visible key
+    auto mask = [&](f32x16_t& a0, f32x16_t& a1) {
+      if (edge) {
+        const int last = p.causal ? min(lk - 1, qi + diag) : lk - 1;  // last visible key
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (key > last) s0[r] = -INFINITY;
-        if (key + 32 > last) s1[r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key > last) a0[r] = -INFINITY;
+          if (key + 32 > last) a1[r] = -INFINITY;
+        }
       }
-    }
+    };
+    mask(s0, s1);
 
-    float mx = -INFINITY;
+    // next block's scores on the matrix cores while this block's exps run on the VALU
+    // (past the last block the slot holds zeros and the result is not used)
+    qk((sl + 1) % NS, n0, n1);
+
+    // probabilities against the current reference, packed to bf16 as the B operand of
+    // the second product; returns this lane's sum of them
+    u32x4_t pf[4];
+    auto probs = [&](const f32x16_t& a0, const f32x16_t& a1) {
+      const float mc = (m == -INFINITY ? 0.f : m) * c;
+      float rs = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
-    mx = halves_max(mx);
-    // move the reference only when some row of the wave grew past the threshold
-    if (__builtin_amdgcn_ballot_w64(mx > m + thresh || (m == -INFINITY && mx != -INFINITY))) {
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(fmaf(a0[r], c, -mc)), p1 = fast_exp2(fmaf(a0[r + 1], c, -mc));
+        const float p2 = fast_exp2(fmaf(a1[r], c, -mc)), p3 = fast_exp2(fmaf(a1[r + 1], c, -mc));
+        rs += (p0 + p1) + (p2 + p3);
+        pf[r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
+        pf[2 + (r >> 3)][(r & 7) >> 1] = pack_bf16(p2, p3);
+      }
+      return rs;
+    };
+    float rs = probs(s0, s1);
+    // The reference is kept while every lane's block sum stays within the bound (so
+    // no probability exceeds it).  Otherwise -- and always on the first block, where
+    // there is no reference yet -- the scores are recomputed from the K block still in
+    // its slot, the reference moves to the row maximum, and the running sum and the
+    // accumulator are rescaled.  The test also catches inf and NaN sums.
+    if (j == 0 || __builtin_amdgcn_ballot_w64(!(rs <= kMaxBlockSum))) {
+      asm volatile("" ::: "memory");  // keep this path's LDS reads off the common path
+      qk(sl, s0, s1);
+      mask(s0, s1);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
+      mx = halves_max(mx);
       const float m_new = fmaxf(m, mx);
       const float alpha = m == -INFINITY ? 0.f : fast_exp2((m - m_new) * c);
       l *= alpha;
 #pragma unroll
       for (int d = 0; d < T::DB; ++d) acc[d] *= alpha;
       m = m_new;
-    }
-    const float mc = (m == -INFINITY ? 0.f : m) * c;
-
-    // next block's scores on the matrix cores while this block's exps run on the VALU
-    // (past the last block the slot holds zeros and the result is not used)
-    qk((j + 1) % NS, n0, n1);
-
-    u32x4_t pf[4];
-    float rs = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = fast_exp2(fmaf(s0[r], c, -mc)), p1 = fast_exp2(fmaf(s0[r + 1], c, -mc));
-      const float p2 = fast_exp2(fmaf(s1[r], c, -mc)), p3 = fast_exp2(fmaf(s1[r + 1], c, -mc));
-      rs += (p0 + p1) + (p2 + p3);
-      pf[r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
-      pf[2 + (r >> 3)][(r & 7) >> 1] = pack_bf16(p2, p3);
+      rs = probs(s0, s1);
     }
     l += rs;
 
     // O^T += V^T P^T; k-step ts holds keys 16 ts + 8 (e/4) + 4 hi + e%4 (e = 0..7)
-    const uint32_t va = vring_addr + (j % NS) * T::TBYTES + vlane;
 #pragma unroll
     for (int d = 0; d < T::DB; ++d) {
-      const uint32_t a = va + 64 * (d ^ vsw);
+      const uint32_t a = vaddr[d];
       u32x2_t v[4][2];
-      lds_read_tr16x2<0, 8 * T::ROWB>(v[0][0], v[0][1], a);
-      lds_read_tr16x2<16 * T::ROWB, 24 * T::ROWB>(v[1][0], v[1][1], a);
-      lds_read_tr16x2<32 * T::ROWB, 40 * T::ROWB>(v[2][0], v[2][1], a);
-      lds_read_tr16x2<48 * T::ROWB, 56 * T::ROWB>(v[3][0], v[3][1], a);
+      lds_read_tr16x2<vo, vo + 8 * T::ROWB>(v[0][0], v[0][1], a);
+      lds_read_tr16x2<vo + 16 * T::ROWB, vo + 24 * T::ROWB>(v[1][0], v[1][1], a);
+      lds_read_tr16x2<vo + 32 * T::ROWB, vo + 40 * T::ROWB>(v[2][0], v[2][1], a);
+      lds_read_tr16x2<vo + 48 * T::ROWB, vo + 56 * T::ROWB>(v[3][0], v[3][1], a);
       lds_wait_tr(v[0][0], v[0][1], v[1][0], v[1][1]);
       lds_wait_tr(v[2][0], v[2][1], v[3][0], v[3][1]);
 #pragma unroll
@@ -278,12 +310,18 @@ fwd_bf16_kernel(FwdParams p) {
   FA_WAIT_LGKMCNT0();  // K slot 0 is refilled at the top of the first block:
   __syncthreads();     // every wave's reads of it must be done
 
+  // NS blocks per trip, so every slot index is a constant; the score registers alternate
+  static_assert(NS == 4, "the unrolled loop below walks four slots");
   int j = 0;
-  for (; j + 1 < nblk; j += 2) {  // two blocks per trip: the score registers alternate
-    step(j, sa0, sa1, sb0, sb1);
-    step(j + 1, sb0, sb1, sa0, sa1);
+  for (; j + 3 < nblk; j += 4) {
+    step(j, Slot<0>{}, sa0, sa1, sb0, sb1);
+    step(j + 1, Slot<1>{}, sb0, sb1, sa0, sa1);
+    step(j + 2, Slot<2>{}, sa0, sa1, sb0, sb1);
+    step(j + 3, Slot<3>{}, sb0, sb1, sa0, sa1);
   }
-  if (j < nblk) step(j, sa0, sa1, sb0, sb1);
+  if (j < nblk) step(j, Slot<0>{}, sa0, sa1, sb0, sb1);
+  if (j + 1 < nblk) step(j + 1, Slot<1>{}, sb0, sb1, sa0, sa1);
+  if (j + 2 < nblk) step(j + 2, Slot<2>{}, sa0, sa1, sb0, sb1);
 
   // ---- epilogue: O = acc / l once; LSE = m * scale + ln(l)
   const float lt = halves_sum(l);
