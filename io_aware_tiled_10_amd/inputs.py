@@ -110,3 +110,69 @@ def decode_inputs(Bs: int, Hq: int, Hkv: int, D: int, len_lo: int, len_hi: int,
     lens = rng.integers(len_lo, len_hi, endpoint=True, size=Bs).astype(np.int64)
     q = bf16_round(rng.standard_normal((Bs, Hq, D), dtype=np.float32))
     return DecodeInputs(lens, q, Hkv, D, seed)
+
+
+def ragged_lengths(B: int, lo: int, hi: int, seed: int = 0) -> np.ndarray:
+    """B sequence lengths drawn uniformly from [lo, hi] (int64)."""
+    return np.random.default_rng([seed, 7]).integers(lo, hi, endpoint=True, size=B).astype(np.int64)
+
+
+def offsets(lens) -> np.ndarray:
+    """Prefix offsets [0, l0, l0 + l1, ...] of a packed batch (int32)."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lens, dtype=np.int64))]).astype(np.int32)
+
+
+@dataclass
+class VarlenInputs:
+    """A packed batch: q [Tq, Hq, D], k and v [Tk, Hkv, D], offsets cu_q, cu_k [B + 1]."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    cu_q: np.ndarray
+    cu_k: np.ndarray
+
+
+def varlen_inputs(lens_q, lens_k, Hq: int, Hkv: int, D: int, dtype: str = "bf16",
+                  seed: int = 0) -> VarlenInputs:
+    rng = np.random.default_rng([seed, 5])
+    cu_q, cu_k = offsets(lens_q), offsets(lens_k)
+    q = _draw(rng, (int(cu_q[-1]), Hq, D), dtype)
+    k = _draw(rng, (int(cu_k[-1]), Hkv, D), dtype)
+    v = _draw(rng, (int(cu_k[-1]), Hkv, D), dtype)
+    return VarlenInputs(q, k, v, cu_q, cu_k)
+
+
+@dataclass
+class PagedCache:
+    """KV cache scattered over physical pages in a random order.
+
+    k_pages, v_pages [P, Hkv, page_size, D]; block_table [Bs, W] int32, entry j of
+    row s naming the page that holds positions j*page_size .. of sequence s, and -1
+    past the sequence.  Rows of a page past its sequence's length hold ``pad_value``.
+    """
+    k_pages: np.ndarray
+    v_pages: np.ndarray
+    block_table: np.ndarray
+    page_size: int
+
+
+def paged_cache(dec: DecodeInputs, page_size: int, seed: int = 0, spare_pages: int = 0,
+                pad_value: float = np.nan) -> PagedCache:
+    lens = [int(x) for x in dec.seq_lens]
+    npg = [(L + page_size - 1) // page_size for L in lens]
+    total = sum(npg) + spare_pages
+    perm = np.random.default_rng([seed, 9]).permutation(total).astype(np.int32)
+    kp = np.full((total, dec.Hkv, page_size, dec.D), pad_value, dtype=np.float32)
+    vp = np.full_like(kp, pad_value)
+    table = np.full((len(lens), max(npg + [1])), -1, dtype=np.int32)
+    nxt = 0
+    for s, L in enumerate(lens):
+        k, v = dec.kv(s)
+        for j in range(npg[s]):
+            page = perm[nxt]
+            nxt += 1
+            table[s, j] = page
+            n = min(page_size, L - j * page_size)
+            kp[page, :, :n] = k[:, j * page_size:j * page_size + n]
+            vp[page, :, :n] = v[:, j * page_size:j * page_size + n]
+    return PagedCache(kp, vp, table, page_size)

@@ -7,7 +7,9 @@ leg import this package.  It shares no code with the HIP library.
 from .attention import (  # noqa: F401
     attn_bwd,
     attn_decode,
+    attn_decode_paged,
     attn_fwd,
+    attn_fwd_varlen,
     decode_split_partials,
     materialised_score_bytes,
     merge_partials,

@@ -38,6 +38,11 @@ Readings taken where the pages are silent (each listed in the design doc):
   result.
 * GQA groups are contiguous: query head hq reads KV head hq // (Hq // Hkv).
 * A query row with no visible key has O = 0 and LSE = -inf; its gradients are 0.
+* Packed variable-length batches: sequence b owns query rows cu_q[b]..cu_q[b+1]
+  and key rows cu_k[b]..cu_k[b+1] of the packed tensors and sees only its own
+  keys; the causal alignment is per sequence.  LSE is laid out [Hq, total rows].
+* Paged KV cache: cached position t of sequence s is row t % page_size of the
+  physical page block_table[s][t // page_size].
 
 All arithmetic is float64.  Inputs given in bf16 / fp32 are upcast exactly.
 """
@@ -54,6 +59,8 @@ __all__ = [
     "attn_fwd",
     "attn_bwd",
     "attn_decode",
+    "attn_fwd_varlen",
+    "attn_decode_paged",
     "online_softmax_attention",
     "decode_split_partials",
     "merge_partials",
@@ -239,6 +246,68 @@ def attn_decode(q, k_cache, v_cache, seq_lens: Sequence[int],
             p, l_ = _softmax_rows(sc[None, :], np.ones((1, ls), dtype=bool))
             o[n, h] = (p @ vh)[0]
             lse[n, h] = l_[0]
+    return o, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_q: Sequence[int], cu_k: Sequence[int],
+                    scale: Optional[float] = None, causal: bool = False
+                    ) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention over a packed batch of variable-length sequences (no padding).
+
+    q [Tq, Hq, D]; k, v [Tk, Hkv, D]; cu_q, cu_k [B+1] non-decreasing offsets
+    (cu[0] = 0, cu[B] = T).  Sequence b attends with its own rows only; each
+    sequence is the plain forward of ``attn_fwd`` on its slice (self-test page,
+    section C: padding and variable-length sequences).  Returns O [Tq, Hq, D] and
+    LSE [Hq, Tq].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    tq, hq_, d = q.shape
+    o = np.zeros((tq, hq_, d))
+    lse = np.full((hq_, tq), -np.inf)
+    for b in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
+        if q1 <= q0:
+            continue
+        qb = q[q0:q1].transpose(1, 0, 2)[None]
+        kb = k[k0:k1].transpose(1, 0, 2)[None]
+        vb = v[k0:k1].transpose(1, 0, 2)[None]
+        ob, lb = attn_fwd(qb, kb, vb, scale, causal)
+        o[q0:q1] = ob[0].transpose(1, 0, 2)
+        lse[:, q0:q1] = lb[0]
+    return o, lse
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens: Sequence[int],
+                      scale: Optional[float] = None, seqs: Optional[Sequence[int]] = None):
+    """One-token decode over a paged KV cache.
+
+    k_pages, v_pages [P, Hkv, page_size, D]; block_table [Bs, W] page ids.  The
+    cached keys of sequence s are gathered in position order -- position t is
+    row t % page_size of page block_table[s][t // page_size] -- and the plain
+    decode of ``attn_decode`` is taken over them (self-test page, section F, why a
+    paged KV cache still needs its own decode path; interview answer, 追问 2, the
+    blocked computation reading paged KV blocks directly).
+    """
+    k_pages, v_pages = np.asarray(k_pages), np.asarray(v_pages)
+    q = _f64(q)
+    ps = k_pages.shape[2]
+    bs, hq_, d = q.shape
+    hkv = k_pages.shape[1]
+    seqs = list(range(bs)) if seqs is None else list(seqs)
+    o = np.zeros((len(seqs), hq_, d))
+    lse = np.full((len(seqs), hq_), -np.inf)
+    for n_, s_ in enumerate(seqs):
+        ls = max(int(seq_lens[s_]), 0)
+        kd = np.zeros((1, hkv, ls, d))
+        vd = np.zeros((1, hkv, ls, d))
+        for j in range((ls + ps - 1) // ps):  # positions j*ps .. of page block_table[s][j]
+            page = int(block_table[s_][j])
+            n = min(ps, ls - j * ps)
+            kd[0, :, j * ps:j * ps + n] = k_pages[page, :, :n]
+            vd[0, :, j * ps:j * ps + n] = v_pages[page, :, :n]
+        o_s, l_s = attn_decode(q[s_:s_ + 1], kd, vd, [ls], scale)
+        o[n_], lse[n_] = o_s[0], l_s[0]
     return o, lse
 
 

@@ -42,3 +42,28 @@ def test_decode_inputs_lengths_and_per_sequence_regeneration():
     kc, vc = small.dense_cache(lmax=10)
     assert np.isnan(kc[1, :, int(small.seq_lens[1]):]).all()
     np.testing.assert_array_equal(kc[1, :, :int(small.seq_lens[1])], k1)
+
+
+def test_varlen_offsets_and_shapes():
+    x = inputs.varlen_inputs([3, 0, 5], [4, 2, 5], 4, 2, 8, "bf16", seed=1)
+    np.testing.assert_array_equal(x.cu_q, [0, 3, 3, 8])
+    np.testing.assert_array_equal(x.cu_k, [0, 4, 6, 11])
+    assert x.q.shape == (8, 4, 8) and x.k.shape == (11, 2, 8) and x.v.shape == (11, 2, 8)
+    np.testing.assert_array_equal(inputs.bf16_round(x.q), x.q)
+
+
+def test_paged_cache_places_every_position_once():
+    dec = inputs.decode_inputs(4, 4, 2, 8, 1, 50, seed=2)
+    pc = inputs.paged_cache(dec, 16, seed=3, spare_pages=5)
+    used = []
+    for s, L in enumerate(dec.seq_lens):
+        k, v = dec.kv(s)
+        n = (int(L) + 15) // 16
+        assert np.all(pc.block_table[s, n:] == -1)
+        for t in range(int(L)):
+            page = pc.block_table[s, t // 16]
+            np.testing.assert_array_equal(pc.k_pages[page, :, t % 16], k[:, t])
+            np.testing.assert_array_equal(pc.v_pages[page, :, t % 16], v[:, t])
+        used += list(pc.block_table[s, :n])
+    assert len(set(used)) == len(used)
+    assert pc.k_pages.shape[0] == len(used) + 5
