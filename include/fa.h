@@ -19,6 +19,18 @@
  *              partials are merged by the online-softmax update.
  *              Pages: interview answer, 高频追问 2; self-test page, section F.
  *
+ * Two variants change only how rows are addressed:
+ *
+ *   fa_fwd_varlen    the forward over a packed batch of variable-length sequences
+ *                    (prefix offsets instead of padding).
+ *                    Pages: self-test page, section C (padding masks and variable-length
+ *                    sequences).
+ *   fa_decode_paged  the split-KV decode over a KV cache kept in fixed-size pages named
+ *                    by a per-sequence block table, read page by page where it lies.
+ *                    Pages: self-test page, section F (why paged attention or a decode
+ *                    kernel is still needed); interview answer, 高频追问 2 (blocked decode
+ *                    reading the paged KV blocks directly).
+ *
  * Conventions shared by every call
  * --------------------------------
  *  * Tensors are [batch, heads, seq, dim] (self-test page section A; the article's
@@ -190,6 +202,85 @@ typedef struct fa_decode_args {
 size_t fa_decode_workspace_bytes(const fa_decode_args *args);
 fa_status fa_decode(const fa_decode_args *args, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Forward over a packed batch of B variable-length sequences (bf16, D in {64, 128}).
+ *   q  [total_q, Hq,  D] bf16 (device); rows cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1
+ *      are the queries of sequence b
+ *   k  [total_k, Hkv, D] bf16 (device); rows cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1
+ *      are the keys of sequence b; v likewise
+ *   cu_seqlens_q, cu_seqlens_k  [B + 1] int32 (device): non-decreasing row offsets with
+ *      [0] = 0 and [B] = total; on the device each is clamped into [previous, total],
+ *      so no read or write leaves the packed tensors whatever they hold
+ *   max_seqlen_q  host-side bound on every sequence's query count (sizes the grid);
+ *      rows of a longer sequence past it are not written
+ *   o  [total_q, Hq, D] out_dtype (device, written); lse contiguous [Hq, total_q] fp32
+ *      (device, written) or NULL
+ *   strides: elements between consecutive rows ([0]) and heads ([1]); dim stride 1.
+ * Each sequence attends its own keys only; causal alignment, GQA, scale and LSE follow
+ * the forward.  A sequence with no keys gets O = 0, LSE = -inf.  k and v may be NULL
+ * when total_k == 0.  Supported: in_dtype FA_BF16, out_dtype FA_BF16 or FA_F32.
+ * ------------------------------------------------------------------------------- */
+typedef struct fa_fwd_varlen_args {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const int32_t *cu_seqlens_q, *cu_seqlens_k;
+  int64_t q_stride[2]; /* elements: row, head */
+  int64_t k_stride[2];
+  int64_t v_stride[2];
+  int64_t o_stride[2];
+  int32_t B, Hq, Hkv, D;
+  int32_t total_q, total_k;
+  int32_t max_seqlen_q;
+  int32_t in_dtype;  /* FA_BF16 */
+  int32_t out_dtype; /* FA_BF16 or FA_F32 */
+  float scale;
+  int32_t causal;
+} fa_fwd_varlen_args;
+
+fa_status fa_fwd_varlen(const fa_fwd_varlen_args *args, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Split-KV decode over a paged KV cache (bf16, D in {64, 128}).
+ *   k_pages, v_pages  page pools of num_pages pages (device), addressed by element
+ *      strides k_stride = {page, head, row within the page}; dim stride 1.  Both
+ *      [num_pages, Hkv, page_size, D] and [num_pages, page_size, Hkv, D] fit.
+ *   block_table  int32 (device), row s at block_table + s * table_stride: entry j names
+ *      the page holding positions j*page_size .. (j+1)*page_size - 1 of sequence s.
+ *      Entries at or past ceil(L_s / page_size) are never read; an entry outside
+ *      [0, num_pages) reads its page as zeros (no memory outside the pools is touched).
+ *   page_size  a power of two, 16 .. 2^20
+ *   max_pages_per_seq  usable entries per table row: max_len <= max_pages_per_seq *
+ *      page_size, table_stride >= max_pages_per_seq
+ *   q, seq_lens, o, lse, max_len, split_len, dtypes and scale as in fa_decode.
+ * Workspace: fa_decode_paged_workspace_bytes() bytes of chunk partials, merged as in
+ * fa_decode.  A sequence with L_s = 0 gets O = 0, LSE = -inf.
+ * ------------------------------------------------------------------------------- */
+typedef struct fa_decode_paged_args {
+  const void *q;
+  const void *k_pages, *v_pages;
+  const int32_t *block_table;
+  const int32_t *seq_lens;
+  void *o;
+  float *lse;
+  int64_t q_stride[2]; /* elements: sequence, head */
+  int64_t k_stride[3]; /* elements: page, head, row within the page */
+  int64_t v_stride[3];
+  int64_t o_stride[2];
+  int64_t table_stride; /* elements between block_table rows */
+  int32_t Bs, Hq, Hkv, D;
+  int32_t num_pages, page_size, max_pages_per_seq;
+  int32_t max_len;
+  int32_t split_len;
+  int32_t in_dtype;  /* FA_BF16 */
+  int32_t out_dtype; /* FA_BF16 or FA_F32 */
+  float scale;
+} fa_decode_paged_args;
+
+size_t fa_decode_paged_workspace_bytes(const fa_decode_paged_args *args);
+fa_status fa_decode_paged(const fa_decode_paged_args *args, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *fa_status_str(int status);

@@ -1,10 +1,13 @@
 """Exact IO-aware attention for MI355X (gfx950): forward, recompute backward and
-split-KV decode, as hand-written HIP kernels behind the C ABI in include/fa.h.
+split-KV decode (contiguous or paged KV cache) and a packed variable-length
+forward, as hand-written HIP kernels behind the C ABI in include/fa.h.
 
 Python-side this package only marshals arguments (``binding``) and draws seeded
 synthetic inputs (``inputs``).
 """
 
-from .binding import FaError, bwd, decode, device_supported, fwd, lib  # noqa: F401
+from .binding import (FaError, bwd, decode, decode_paged, device_supported, fwd,  # noqa: F401
+                      fwd_varlen, lib)
 
-__all__ = ["fwd", "bwd", "decode", "device_supported", "lib", "FaError"]
+__all__ = ["fwd", "fwd_varlen", "bwd", "decode", "decode_paged", "device_supported", "lib",
+           "FaError"]

@@ -62,7 +62,36 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
-EXPORTED = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_workspace_bytes",
+class FwdVarlenArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+        ("q_stride", c_i64x2), ("k_stride", c_i64x2), ("v_stride", c_i64x2), ("o_stride", c_i64x2),
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("total_q", ctypes.c_int32), ("total_k", ctypes.c_int32), ("max_seqlen_q", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
+    ]
+
+
+class DecodePagedArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("q_stride", c_i64x2), ("k_stride", c_i64x3), ("v_stride", c_i64x3), ("o_stride", c_i64x2),
+        ("table_stride", ctypes.c_int64),
+        ("Bs", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32), ("max_len", ctypes.c_int32),
+        ("split_len", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+EXPORTED = ["fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode",
+            "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
             "fa_status_str", "fa_device_supported", "fa_version"]
 
 _lib = None
@@ -87,6 +116,13 @@ def lib() -> ctypes.CDLL:
         h.fa_decode.restype = ctypes.c_int
         h.fa_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
         h.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+        h.fa_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs), ctypes.c_void_p]
+        h.fa_fwd_varlen.restype = ctypes.c_int
+        h.fa_decode_paged.argtypes = [ctypes.POINTER(DecodePagedArgs), ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p]
+        h.fa_decode_paged.restype = ctypes.c_int
+        h.fa_decode_paged_workspace_bytes.argtypes = [ctypes.POINTER(DecodePagedArgs)]
+        h.fa_decode_paged_workspace_bytes.restype = ctypes.c_size_t
         h.fa_status_str.argtypes = [ctypes.c_int]
         h.fa_status_str.restype = ctypes.c_char_p
         h.fa_device_supported.argtypes = [ctypes.c_int]
@@ -153,6 +189,44 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if with_lse else None)
     a = fwd_args(q, k, v, o, lse, causal, scale, kv_lens)
     _check(lib().fa_fwd(ctypes.byref(a), _stream(q.device)))
+    return o, lse
+
+
+def _s2(t: torch.Tensor):
+    if t.stride(-1) != 1:
+        raise ValueError("the last (head) dimension must be contiguous")
+    return c_i64x2(*t.stride()[:2])
+
+
+def fwd_varlen_args(q, k, v, o, lse, cu_q, cu_k, max_seqlen_q, causal, scale) -> FwdVarlenArgs:
+    Tq, Hq, D = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    return FwdVarlenArgs(
+        q=_ptr(q), k=_ptr(k), v=_ptr(v), o=_ptr(o), lse=_ptr(lse),
+        cu_seqlens_q=_ptr(cu_q), cu_seqlens_k=_ptr(cu_k),
+        q_stride=_s2(q), k_stride=_s2(k), v_stride=_s2(v), o_stride=_s2(o),
+        B=cu_q.numel() - 1, Hq=Hq, Hkv=Hkv, D=D, total_q=Tq, total_k=Tk,
+        max_seqlen_q=int(max_seqlen_q), in_dtype=_DT[q.dtype], out_dtype=_DT[o.dtype],
+        scale=_scale(scale, D), causal=int(bool(causal)))
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+               cu_seqlens_k: torch.Tensor, max_seqlen_q: int, causal: bool = False,
+               scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+               with_lse: bool = True, out: Optional[torch.Tensor] = None,
+               lse_out: Optional[torch.Tensor] = None):
+    """Packed variable-length forward via ``fa_fwd_varlen``.
+
+    q [Tq, Hq, D], k/v [Tk, Hkv, D], cu_seqlens_* int32 [B+1] on the device; returns
+    O [Tq, Hq, D] and LSE [Hq, Tq].
+    """
+    Tq, Hq, D = q.shape
+    o = out if out is not None else torch.empty((Tq, Hq, D), dtype=out_dtype or q.dtype,
+                                                device=q.device)
+    lse = lse_out if lse_out is not None else (
+        torch.empty((Hq, Tq), dtype=torch.float32, device=q.device) if with_lse else None)
+    a = fwd_varlen_args(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal, scale)
+    _check(lib().fa_fwd_varlen(ctypes.byref(a), _stream(q.device)))
     return o, lse
 
 
@@ -227,6 +301,47 @@ def decode(q, k_cache, v_cache, seq_lens, max_len: Optional[int] = None, split_l
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib().fa_decode(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return o, lse
+
+
+def decode_paged_args(q, k_pages, v_pages, block_table, seq_lens, o, lse, page_size, max_len,
+                      split_len, scale) -> DecodePagedArgs:
+    Bs, Hq, D = q.shape
+    if q.stride(-1) != 1 or o.stride(-1) != 1 or block_table.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return DecodePagedArgs(
+        q=_ptr(q), k_pages=_ptr(k_pages), v_pages=_ptr(v_pages), block_table=_ptr(block_table),
+        seq_lens=_ptr(seq_lens), o=_ptr(o), lse=_ptr(lse),
+        q_stride=c_i64x2(*q.stride()[:2]), k_stride=_s3(k_pages), v_stride=_s3(v_pages),
+        o_stride=c_i64x2(*o.stride()[:2]), table_stride=block_table.stride(0),
+        Bs=Bs, Hq=Hq, Hkv=k_pages.shape[1], D=D, num_pages=k_pages.shape[0],
+        page_size=int(page_size), max_pages_per_seq=block_table.shape[1], max_len=int(max_len),
+        split_len=int(split_len), in_dtype=_DT[q.dtype], out_dtype=_DT[o.dtype],
+        scale=_scale(scale, D))
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, max_len: int, split_len: int = 2048,
+                 scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+                 with_lse: bool = True, workspace: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None):
+    """Split-KV decode over a paged cache via ``fa_decode_paged``.
+
+    q [Bs, Hq, D]; k_pages / v_pages indexed [page, head, row, D] through their strides
+    (a [P, page, Hkv, D] pool passes ``pool.transpose(1, 2)``); block_table int32 [Bs, W];
+    the page size is ``k_pages.shape[2]``.
+    """
+    Bs, Hq, D = q.shape
+    o = out if out is not None else torch.empty((Bs, Hq, D), dtype=out_dtype or q.dtype,
+                                                device=q.device)
+    lse = lse_out if lse_out is not None else (
+        torch.empty((Bs, Hq), dtype=torch.float32, device=q.device) if with_lse else None)
+    a = decode_paged_args(q, k_pages, v_pages, block_table, seq_lens, o, lse, k_pages.shape[2],
+                          max_len, split_len, scale)
+    need = lib().fa_decode_paged_workspace_bytes(ctypes.byref(a))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().fa_decode_paged(ctypes.byref(a), _ptr(workspace), workspace.numel(),
+                                 _stream(q.device)))
     return o, lse
 
 

@@ -89,6 +89,33 @@ fa_status validate_bwd(const fa_bwd_args* a) {
   return FA_OK;
 }
 
+fa_status validate_fwd_varlen(const fa_fwd_varlen_args* a) {
+  if (!a) return FA_ERR_NULL_PTR;
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->D < 1) return FA_ERR_SHAPE;
+  if (a->total_q < 0 || a->total_k < 0 || a->max_seqlen_q < 0 || a->max_seqlen_q > a->total_q)
+    return FA_ERR_SHAPE;
+  if (a->Hq > kMaxHeads || a->Hkv > a->Hq || a->Hq % a->Hkv != 0) return FA_ERR_SHAPE;
+  if (a->in_dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (a->out_dtype != FA_BF16 && a->out_dtype != FA_F32) return FA_ERR_DTYPE;
+  if (a->D != 64 && a->D != 128) return FA_ERR_UNSUPPORTED;
+  if (!scale_ok(a->scale)) return FA_ERR_ARG;
+  if (a->causal != 0 && a->causal != 1) return FA_ERR_ARG;
+  if (a->total_q == 0 || a->max_seqlen_q == 0) return FA_OK;
+  if (!a->q || !a->o || !a->cu_seqlens_q || !a->cu_seqlens_k) return FA_ERR_NULL_PTR;
+  if (a->total_k > 0 && (!a->k || !a->v)) return FA_ERR_NULL_PTR;
+  const int ob = a->out_dtype == FA_BF16 ? 2 : 4;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return FA_ERR_STRIDE;
+  if (!strides_ok(a->q_stride, 2, 2) || !strides_ok(a->k_stride, 2, 2) ||
+      !strides_ok(a->v_stride, 2, 2) || !strides_ok(a->o_stride, 2, ob))
+    return FA_ERR_STRIDE;
+  if ((reinterpret_cast<uintptr_t>(a->cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(a->cu_seqlens_k) & 3u))
+    return FA_ERR_STRIDE;
+  if (a->lse && (reinterpret_cast<uintptr_t>(a->lse) & 3u)) return FA_ERR_STRIDE;
+  return FA_OK;
+}
+
 int decode_nsplit(const fa_decode_args* a) {
   return a->max_len <= 0 ? 0 : (a->max_len + a->split_len - 1) / a->split_len;
 }
@@ -120,6 +147,53 @@ fa_status validate_decode(const fa_decode_args* a) {
   return FA_OK;
 }
 
+int paged_nsplit(const fa_decode_paged_args* a) {
+  return a->max_len <= 0 ? 0 : (a->max_len + a->split_len - 1) / a->split_len;
+}
+
+int log2_exact(int x) {  // log2 of a power of two, else -1
+  if (x <= 0 || (x & (x - 1)) != 0) return -1;
+  int n = 0;
+  while ((1 << n) != x) ++n;
+  return n;
+}
+
+fa_status validate_decode_paged(const fa_decode_paged_args* a) {
+  if (!a) return FA_ERR_NULL_PTR;
+  if (a->Bs < 0 || a->Bs > kMaxGridYZ || a->Hq < 1 || a->Hkv < 1 || a->D < 1) return FA_ERR_SHAPE;
+  if (a->Hq > kMaxHeads || a->Hkv > a->Hq || a->Hq % a->Hkv != 0) return FA_ERR_SHAPE;
+  const int lp = log2_exact(a->page_size);
+  if (lp < 4 || lp > 20) return FA_ERR_SHAPE;
+  if (a->num_pages < 0 || a->max_pages_per_seq < 0 || a->max_len < 0) return FA_ERR_SHAPE;
+  if ((int64_t)a->max_len > (int64_t)a->max_pages_per_seq * a->page_size) return FA_ERR_SHAPE;
+  if (a->table_stride < a->max_pages_per_seq) return FA_ERR_SHAPE;
+  if (a->split_len < 128 || a->split_len % 128 != 0) return FA_ERR_SHAPE;
+  if (a->in_dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (a->out_dtype != FA_BF16 && a->out_dtype != FA_F32) return FA_ERR_DTYPE;
+  if (a->D != 64 && a->D != 128) return FA_ERR_UNSUPPORTED;
+  if (!scale_ok(a->scale)) return FA_ERR_ARG;
+  const int64_t nhb = (a->Hq / a->Hkv + 31) / 32;
+  if ((int64_t)a->Hkv * nhb > kMaxGridYZ) return FA_ERR_SHAPE;
+  if ((int64_t)paged_nsplit(a) * nhb * a->Hkv * a->Bs > 0x7fffffff) return FA_ERR_SHAPE;
+  if (a->Bs == 0) return FA_OK;
+  if (!a->q || !a->o || !a->seq_lens) return FA_ERR_NULL_PTR;
+  if (a->max_len > 0 && (!a->k_pages || !a->v_pages || !a->block_table)) return FA_ERR_NULL_PTR;
+  const int ob = a->out_dtype == FA_BF16 ? 2 : 4;
+  if (!aligned16(a->q) || !aligned16(a->o)) return FA_ERR_STRIDE;
+  if (a->k_pages && !aligned16(a->k_pages)) return FA_ERR_STRIDE;
+  if (a->v_pages && !aligned16(a->v_pages)) return FA_ERR_STRIDE;
+  if (!strides_ok(a->q_stride, 2, 2) || !strides_ok(a->k_stride, 3, 2) ||
+      !strides_ok(a->v_stride, 3, 2) || !strides_ok(a->o_stride, 2, ob))
+    return FA_ERR_STRIDE;
+  if (reinterpret_cast<uintptr_t>(a->block_table) & 3u) return FA_ERR_STRIDE;
+  // byte offsets inside one page are 32-bit
+  if ((int64_t)a->page_size * a->k_stride[2] * 2 > 0x7fffffff ||
+      (int64_t)a->page_size * a->v_stride[2] * 2 > 0x7fffffff)
+    return FA_ERR_SHAPE;
+  if (a->lse && (reinterpret_cast<uintptr_t>(a->lse) & 3u)) return FA_ERR_STRIDE;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -138,7 +212,34 @@ fa_status fa_fwd(const fa_fwd_args* a, void* stream) {
   p.ks0 = a->k_stride[0], p.ks1 = a->k_stride[1], p.ks2 = a->k_stride[2];
   p.vs0 = a->v_stride[0], p.vs1 = a->v_stride[1], p.vs2 = a->v_stride[2];
   p.os0 = a->o_stride[0], p.os1 = a->o_stride[1], p.os2 = a->o_stride[2];
+  p.lse_sb = (int64_t)a->Hq * a->Nq, p.lse_sh = a->Nq;
   p.B = a->B, p.Hq = a->Hq, p.Hkv = a->Hkv, p.Nq = a->Nq, p.Nk = a->Nk;
+  p.G = a->Hq / a->Hkv;
+  p.scale = a->scale;
+  p.scale_log2 = a->scale * 1.4426950408889634f;
+  p.causal = a->causal;
+  return map_launch_error(
+      fa::launch_fwd(p, a->in_dtype, a->out_dtype, a->D, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd_varlen(const fa_fwd_varlen_args* a, void* stream) {
+  const fa_status st = validate_fwd_varlen(a);
+  if (st != FA_OK || a->total_q == 0 || a->max_seqlen_q == 0) return st;
+  fa::FwdParams p{};
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.k = static_cast<const uint16_t*>(a->k);
+  p.v = static_cast<const uint16_t*>(a->v);
+  p.o = a->o;
+  p.lse = a->lse;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
+  p.total_q = a->total_q, p.total_k = a->total_k;
+  p.qs1 = a->q_stride[1], p.qs2 = a->q_stride[0];
+  p.ks1 = a->k_stride[1], p.ks2 = a->k_stride[0];
+  p.vs1 = a->v_stride[1], p.vs2 = a->v_stride[0];
+  p.os1 = a->o_stride[1], p.os2 = a->o_stride[0];
+  p.lse_sb = 0, p.lse_sh = a->total_q;
+  p.B = a->B, p.Hq = a->Hq, p.Hkv = a->Hkv, p.Nq = a->max_seqlen_q, p.Nk = 0;
   p.G = a->Hq / a->Hkv;
   p.scale = a->scale;
   p.scale_log2 = a->scale * 1.4426950408889634f;
@@ -221,6 +322,46 @@ fa_status fa_decode(const fa_decode_args* a, void* workspace, size_t ws_bytes, v
       fa::launch_decode(p, a->D, a->out_dtype, static_cast<hipStream_t>(stream)));
 }
 
+size_t fa_decode_paged_workspace_bytes(const fa_decode_paged_args* a) {
+  if (validate_decode_paged(a) != FA_OK) return 0;
+  return fa::decode_workspace_bytes(a->Bs, a->Hq, paged_nsplit(a), a->D);
+}
+
+fa_status fa_decode_paged(const fa_decode_paged_args* a, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  const fa_status st = validate_decode_paged(a);
+  if (st != FA_OK || a->Bs == 0) return st;
+  const int nsplit = paged_nsplit(a);
+  const size_t need = fa::decode_workspace_bytes(a->Bs, a->Hq, nsplit, a->D);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return FA_ERR_WORKSPACE;
+  fa::DecParams p{};
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.k = static_cast<const uint16_t*>(a->k_pages);
+  p.v = static_cast<const uint16_t*>(a->v_pages);
+  p.seq_lens = a->seq_lens;
+  p.o = a->o;
+  p.lse = a->lse;
+  const size_t o_bytes = ((size_t)a->Bs * a->Hq * nsplit * a->D * 4 + 255) & ~size_t(255);
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  p.qs0 = a->q_stride[0], p.qs1 = a->q_stride[1];
+  p.ks0 = a->k_stride[0], p.ks1 = a->k_stride[1], p.ks2 = a->k_stride[2];
+  p.vs0 = a->v_stride[0], p.vs1 = a->v_stride[1], p.vs2 = a->v_stride[2];
+  p.os0 = a->o_stride[0], p.os1 = a->o_stride[1];
+  p.Bs = a->Bs, p.Hq = a->Hq, p.Hkv = a->Hkv;
+  p.G = a->Hq / a->Hkv;
+  p.nhb = (p.G + 31) / 32;
+  p.max_len = a->max_len, p.split_len = a->split_len, p.nsplit = nsplit;
+  p.scale = a->scale;
+  p.scale_log2 = a->scale * 1.4426950408889634f;
+  p.table = a->block_table;
+  p.table_stride = a->table_stride;
+  p.page_shift = log2_exact(a->page_size);
+  p.num_pages = a->num_pages;
+  return map_launch_error(
+      fa::launch_decode(p, a->D, a->out_dtype, static_cast<hipStream_t>(stream)));
+}
+
 const char* fa_status_str(int s) {
   switch (s) {
     case FA_OK: return "FA_OK";
@@ -243,6 +384,6 @@ int fa_device_supported(int device) {
   return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
 }
 
-int fa_version(void) { return (1 << 16) | 0; }
+int fa_version(void) { return (1 << 16) | 1; }
 
 }  // extern "C"

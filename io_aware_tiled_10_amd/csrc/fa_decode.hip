@@ -23,7 +23,10 @@
 //    16-byte reads, V feeds O^T += V^T P^T through transposing reads (no register
 //    shuffles and no second LDS pass);
 //  * the four waves' (m, l, acc) are merged through LDS at the end of the chunk;
-//  * chunks past a sequence's length exit at once; keys past it are never loaded.
+//  * chunks past a sequence's length exit at once; keys past it are never loaded;
+//  * a paged cache (interview answer, 高频追问 2: the blocked decode reads the paged KV
+//    blocks where they lie) changes only the descriptors: each 32-key block takes its
+//    page from the block table and the DMA reads the rows straight out of that page.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -56,7 +59,7 @@ struct DecTile {
   static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPB) % (SPR / 4)); }
 };
 
-template <int D>
+template <int D, bool PAGED>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecParams p) {
   using T = DecTile<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[T::LDS_BYTES];
@@ -93,8 +96,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecParams p) {
     for (int k = 0; k < T::KS; ++k) qf[k] = buf_load16(rq, off + 32 * k);
     asm volatile("" ::: "memory");  // issue these before the ring loads below
   }
-  const uint16_t* kb = p.k + s * p.ks0 + hkv * p.ks1;
-  const uint16_t* vb = p.v + s * p.vs0 + hkv * p.vs1;
+  // contiguous cache: this sequence's rows; paged: the head's rows of page 0
+  const uint16_t* kb = p.k + (PAGED ? 0 : s * p.ks0) + hkv * p.ks1;
+  const uint16_t* vb = p.v + (PAGED ? 0 : s * p.vs0) + hkv * p.vs1;
   const int64_t kpitch = p.ks2 * 2, vpitch = p.vs2 * 2;
   unsigned char* ring = lds + wave * T::RING;
 
@@ -127,14 +131,56 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecParams p) {
   // descriptor is empty, nothing is read and the stage is filled with zeros
   auto issue = [&](int n) {
     const int key0 = start + kDecBlock * (wave + kDecWaves * n);
-    const int rows = min(kDecBlock, end - key0);
-    const auto rk = make_rsrc(kb + (int64_t)key0 * p.ks2, rows_span(rows, kpitch, T::ROWB));
-    const auto rv = make_rsrc(vb + (int64_t)key0 * p.vs2, rows_span(rows, vpitch, T::ROWB));
     unsigned char* st = ring + (n & 1) * T::STAGE;
+    if constexpr (!PAGED) {
+      const int rows = min(kDecBlock, end - key0);
+      const auto rk = make_rsrc(kb + (int64_t)key0 * p.ks2, rows_span(rows, kpitch, T::ROWB));
+      const auto rv = make_rsrc(vb + (int64_t)key0 * p.vs2, rows_span(rows, vpitch, T::ROWB));
 #pragma unroll
-    for (int i = 0; i < T::NDMA; ++i) lds_dma16(rk, st + 1024 * i, kdma[i], 1);
+      for (int i = 0; i < T::NDMA; ++i) lds_dma16(rk, st + 1024 * i, kdma[i], 1);
 #pragma unroll
-    for (int i = 0; i < T::NDMA; ++i) lds_dma16(rv, st + T::TBYTES + 1024 * i, vdma[i], 1);
+      for (int i = 0; i < T::NDMA; ++i) lds_dma16(rv, st + T::TBYTES + 1024 * i, vdma[i], 1);
+    } else {
+      // The block's 32 rows lie in one page (pages of >= 32 rows) or in two 16-row
+      // pages (half h = rows 16h ..).  One descriptor per page spans that page's rows
+      // inside the chunk, so rows past the chunk read as zeros, and so does a page whose
+      // id is outside the pool; no table entry is read for a block past the chunk.  A
+      // DMA instruction's RPI rows never straddle a page (RPI <= 16 <= page size).
+      const int psz = 1 << p.page_shift;
+      const bool two = p.page_shift == 4;
+      __amdgpu_buffer_rsrc_t rk[2], rv[2];
+      int pstart[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h == 1 && !two) {
+          rk[1] = rk[0], rv[1] = rv[0], pstart[1] = pstart[0];
+          break;
+        }
+        const int row = key0 + 16 * h;
+        pstart[h] = row & ~(psz - 1);
+        int valid = min(end - pstart[h], psz);
+        int page = 0;
+        if (row < end) page = p.table[s * p.table_stride + (row >> p.page_shift)];
+        if (row >= end || page < 0 || page >= p.num_pages) valid = 0, page = 0;
+        rk[h] = make_rsrc(kb + (int64_t)page * p.ks0, rows_span(valid, kpitch, T::ROWB));
+        rv[h] = make_rsrc(vb + (int64_t)page * p.vs0, rows_span(valid, vpitch, T::ROWB));
+      }
+      // instruction i stages rows RPI*i ..: kdma[i] counts them from key0; for the
+      // second half the 16 rows before its page move from the voffset to the page
+      // start, and the scalar offset adds the rows between the page start and key0
+#pragma unroll
+      for (int i = 0; i < T::NDMA; ++i) {
+        const int h = (T::RPI * i) >= 16 ? 1 : 0;
+        const uint32_t soff = (uint32_t)((key0 + 16 * h - pstart[h]) * kpitch);
+        lds_dma16(rk[h], st + 1024 * i, kdma[i] - (uint32_t)(h * 16 * kpitch), 1, soff);
+      }
+#pragma unroll
+      for (int i = 0; i < T::NDMA; ++i) {
+        const int h = (T::RPI * i) >= 16 ? 1 : 0;
+        const uint32_t soff = (uint32_t)((key0 + 16 * h - pstart[h]) * vpitch);
+        lds_dma16(rv[h], st + T::TBYTES + 1024 * i, vdma[i] - (uint32_t)(h * 16 * vpitch), 1, soff);
+      }
+    }
   };
 
   const int mine = wave < nb ? (nb - wave + kDecWaves - 1) / kDecWaves : 0;
@@ -315,8 +361,12 @@ hipError_t launch_decode(const DecParams& p, int D, int out_dtype, hipStream_t s
     const int64_t n = (int64_t)p.nsplit * p.nhb * p.Hkv * p.Bs;
     if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)n);
-    const hipError_t e = D == 128 ? launch(decode_split_kernel<128>, grid, dim3(256), p, stream)
-                                  : launch(decode_split_kernel<64>, grid, dim3(256), p, stream);
+    const bool paged = p.table != nullptr;
+    const hipError_t e =
+        D == 128 ? (paged ? launch(decode_split_kernel<128, true>, grid, dim3(256), p, stream)
+                          : launch(decode_split_kernel<128, false>, grid, dim3(256), p, stream))
+                 : (paged ? launch(decode_split_kernel<64, true>, grid, dim3(256), p, stream)
+                          : launch(decode_split_kernel<64, false>, grid, dim3(256), p, stream));
     if (e != hipSuccess) return e;
   }
   const dim3 mgrid(p.Bs * p.Hq);

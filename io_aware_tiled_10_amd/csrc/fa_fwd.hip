@@ -35,7 +35,10 @@
 //    maximum, the reference and the rescale done; the common path has no max at all;
 //  * causal: blocks above the diagonal are never visited, the mask is applied only
 //    on blocks that cross it, and the heaviest query tiles are launched first;
-//  * workgroups are ordered so tiles that share a KV head run on the same XCD.
+//  * workgroups are ordered so tiles that share a KV head run on the same XCD;
+//  * a packed batch of variable-length sequences (self-test page, section C) runs the
+//    same kernel: each workgroup takes its sequence's row range from the offsets, and
+//    tiles past a short sequence exit at once.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -102,13 +105,21 @@ fwd_bf16_kernel(FwdParams p) {
   const int qt = p.causal ? p.nqt - 1 - rank : rank;
   const int hq = hkv * p.G + gi;
 
-  int lk = p.Nk;
-  if (p.kv_lens) {
+  // this batch entry's query rows and valid keys; a packed batch takes them from the
+  // offsets (clamped to the packed tensors) and shifts every row index by its first row
+  int nq = p.Nq, lk = p.Nk;
+  int64_t qr0 = 0, kr0 = 0;
+  if (p.cu_q) {
+    const int a0 = min(max(p.cu_q[b], 0), p.total_q), a1 = min(max(p.cu_q[b + 1], a0), p.total_q);
+    const int c0 = min(max(p.cu_k[b], 0), p.total_k), c1 = min(max(p.cu_k[b + 1], c0), p.total_k);
+    nq = a1 - a0, qr0 = a0, lk = c1 - c0, kr0 = c0;
+  } else if (p.kv_lens) {
     lk = p.kv_lens[b];
     lk = lk < 0 ? 0 : (lk > p.Nk ? p.Nk : lk);
   }
-  const int diag = lk - p.Nq;  // key j visible to query i iff j <= i + diag
+  const int diag = lk - nq;  // key j visible to query i iff j <= i + diag
   const int q_wg0 = qt * BR;
+  if (q_wg0 >= nq) return;  // a tile past a short sequence of a packed batch (uniform)
   int kend = lk;
   if (p.causal) {
     const int lim = q_wg0 + BR + diag;  // one past the last key the tile's last row sees
@@ -120,15 +131,16 @@ fwd_bf16_kernel(FwdParams p) {
   const int qi = q_wg0 + wave * 32 + l32;  // this lane's query row
 
   if (nblk == 0) {  // no visible key for any row of the tile: O = 0, LSE = -inf
-    if (qi < p.Nq) {
+    if (qi < nq) {
+      const int64_t orow0 = b * p.os0 + hq * p.os1 + (qr0 + qi) * p.os2;
       if constexpr (OUT_F32) {
-        float* orow = static_cast<float*>(p.o) + b * p.os0 + hq * p.os1 + (int64_t)qi * p.os2;
+        float* orow = static_cast<float*>(p.o) + orow0;
         for (int d = 4 * hi; d < D; d += 8) *reinterpret_cast<f32x4_t*>(orow + d) = f32x4_t{};
       } else {
-        uint16_t* orow = static_cast<uint16_t*>(p.o) + b * p.os0 + hq * p.os1 + (int64_t)qi * p.os2;
+        uint16_t* orow = static_cast<uint16_t*>(p.o) + orow0;
         for (int d = 4 * hi; d < D; d += 8) *reinterpret_cast<u32x2_t*>(orow + d) = u32x2_t{};
       }
-      if (p.lse && hi == 0) p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qi] = -INFINITY;
+      if (p.lse && hi == 0) p.lse[b * p.lse_sb + hq * p.lse_sh + qr0 + qi] = -INFINITY;
     }
     return;  // uniform over the workgroup
   }
@@ -137,16 +149,16 @@ fwd_bf16_kernel(FwdParams p) {
   u32x4_t qf[T::KS];
   {
     const int64_t qpitch = p.qs2 * 2;
-    const uint16_t* qtile = p.q + b * p.qs0 + hq * p.qs1 + (int64_t)q_wg0 * p.qs2;
-    const auto rq = make_rsrc(qtile, rows_span(min(BR, p.Nq - q_wg0), qpitch, D * 2));
+    const uint16_t* qtile = p.q + b * p.qs0 + hq * p.qs1 + (qr0 + q_wg0) * p.qs2;
+    const auto rq = make_rsrc(qtile, rows_span(min(BR, nq - q_wg0), qpitch, D * 2));
     const uint32_t off = (uint32_t)((wave * 32 + l32) * qpitch) + 16 * hi;
 #pragma unroll
     for (int s = 0; s < T::KS; ++s) qf[s] = buf_load16(rq, off + 32 * s);
     asm volatile("" ::: "memory");  // issue these before the ring loads below
   }
 
-  const uint16_t* kbase = p.k + b * p.ks0 + hkv * p.ks1;
-  const uint16_t* vbase = p.v + b * p.vs0 + hkv * p.vs1;
+  const uint16_t* kbase = p.k + b * p.ks0 + hkv * p.ks1 + kr0 * p.ks2;
+  const uint16_t* vbase = p.v + b * p.vs0 + hkv * p.vs1 + kr0 * p.vs2;
   const int64_t kpitch = p.ks2 * 2, vpitch = p.vs2 * 2;
 
   // DMA: thread (wave w, lane) fills, for instruction i, row RPI (NW i + w) + lane / SPR,
@@ -326,9 +338,10 @@ fwd_bf16_kernel(FwdParams p) {
   // ---- epilogue: O = acc / l once; LSE = m * scale + ln(l)
   const float lt = halves_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (qi < p.Nq) {
+  if (qi < nq) {
+    const int64_t orow0 = b * p.os0 + hq * p.os1 + (qr0 + qi) * p.os2;
     if constexpr (OUT_F32) {
-      float* orow = static_cast<float*>(p.o) + b * p.os0 + hq * p.os1 + (int64_t)qi * p.os2;
+      float* orow = static_cast<float*>(p.o) + orow0;
 #pragma unroll
       for (int d = 0; d < T::DB; ++d)
 #pragma unroll
@@ -337,7 +350,7 @@ fwd_bf16_kernel(FwdParams p) {
               f32x4_t{acc[d][4 * rg] * inv, acc[d][4 * rg + 1] * inv, acc[d][4 * rg + 2] * inv,
                       acc[d][4 * rg + 3] * inv};
     } else {
-      uint16_t* orow = static_cast<uint16_t*>(p.o) + b * p.os0 + hq * p.os1 + (int64_t)qi * p.os2;
+      uint16_t* orow = static_cast<uint16_t*>(p.o) + orow0;
 #pragma unroll
       for (int d = 0; d < T::DB; ++d)
 #pragma unroll
@@ -347,7 +360,7 @@ fwd_bf16_kernel(FwdParams p) {
                       pack_bf16(acc[d][4 * rg + 2] * inv, acc[d][4 * rg + 3] * inv)};
     }
     if (p.lse && hi == 0)
-      p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qi] = lt > 0.f ? m * p.scale + __logf(lt) : -INFINITY;
+      p.lse[b * p.lse_sb + hq * p.lse_sh + qr0 + qi] = lt > 0.f ? m * p.scale + __logf(lt) : -INFINITY;
   }
 }
 
@@ -450,7 +463,7 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdParams p) {
     for (int d = 0; d < D; d += 4)
       *reinterpret_cast<f32x4_t*>(orow + d) =
           f32x4_t{acc[d] * inv, acc[d + 1] * inv, acc[d + 2] * inv, acc[d + 3] * inv};
-    if (p.lse) p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qi] = l > 0.f ? m * p.scale + __logf(l) : -INFINITY;
+    if (p.lse) p.lse[b * p.lse_sb + hq * p.lse_sh + qi] = l > 0.f ? m * p.scale + __logf(l) : -INFINITY;
   }
 }
 

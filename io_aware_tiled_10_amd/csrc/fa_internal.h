@@ -14,8 +14,14 @@ struct FwdParams {
   void* o;
   float* lse;
   const int32_t* kv_lens;
+  // packed variable-length batch: sequence b owns rows cu_q[b] .. cu_q[b+1] of q / o
+  // and cu_k[b] .. cu_k[b+1] of k / v (batch strides unused); NULL for [B, H, N, D]
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
   int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
-  int B, Hq, Hkv, Nq, Nk, G, nqt;
+  int64_t lse_sb, lse_sh;  // LSE element of (b, h, row): b * lse_sb + h * lse_sh + row
+  int B, Hq, Hkv, Nq, Nk, G, nqt;  // packed batches: Nq = longest sequence
   float scale, scale_log2;
   int causal;
 };
@@ -53,6 +59,12 @@ struct DecParams {
   int64_t qs0, qs1, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1;
   int Bs, Hq, Hkv, G, nhb, max_len, split_len, nsplit;
   float scale, scale_log2;
+  // paged cache (NULL table: contiguous [Bs, Hkv, cache_len, D]): k / v point at the
+  // page pool, ks0 / vs0 are page strides, position t of sequence s is row
+  // t % 2^page_shift of page table[s * table_stride + (t >> page_shift)]
+  const int32_t* table;
+  int64_t table_stride;
+  int page_shift, num_pages;
 };
 
 size_t decode_workspace_bytes(int Bs, int Hq, int nsplit, int D);

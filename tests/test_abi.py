@@ -158,3 +158,77 @@ def test_decode_workspace_query():
     assert need == rows * 128 * 4 + rows * 4
     assert fb.lib().fa_decode(ctypes.byref(a), FAKE, need - 1, None) == WS
     assert fb.lib().fa_decode(ctypes.byref(good_dec(Bs=0)), None, 0, None) == OK
+
+
+def good_varlen(**kw):
+    a = fb.FwdVarlenArgs(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu_seqlens_q=FAKE, cu_seqlens_k=FAKE,
+                         q_stride=fb.c_i64x2(4 * 128, 128), k_stride=fb.c_i64x2(2 * 128, 128),
+                         v_stride=fb.c_i64x2(2 * 128, 128), o_stride=fb.c_i64x2(4 * 128, 128),
+                         B=3, Hq=4, Hkv=2, D=128, total_q=100, total_k=120, max_seqlen_q=60,
+                         in_dtype=fb.FA_BF16, out_dtype=fb.FA_BF16, scale=0.088, causal=1)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+VARLEN_BAD = [
+    ({"B": 0}, SHAPE), ({"Hq": 3}, SHAPE), ({"total_q": -1}, SHAPE), ({"max_seqlen_q": 101}, SHAPE),
+    ({"total_k": -5}, SHAPE), ({"D": 96}, UNSUP), ({"in_dtype": fb.FA_F32, "out_dtype": fb.FA_F32}, DTYPE),
+    ({"out_dtype": 4}, DTYPE), ({"scale": 0.0}, ARG), ({"causal": 3}, ARG),
+    ({"cu_seqlens_q": None}, NULL), ({"cu_seqlens_k": None}, NULL), ({"k": None}, NULL),
+    ({"q": FAKE + 8}, STRIDE), ({"cu_seqlens_k": FAKE + 2}, STRIDE),
+    ({"k_stride": fb.c_i64x2(2 * 128, 3)}, STRIDE), ({"lse": FAKE + 1}, STRIDE),
+]
+
+
+@pytest.mark.parametrize("change,status", VARLEN_BAD)
+def test_fwd_varlen_rejects_bad_arguments(change, status):
+    assert fb.lib().fa_fwd_varlen(ctypes.byref(good_varlen(**change)), None) == status
+
+
+def test_fwd_varlen_empty_batches_launch_nothing():
+    assert fb.lib().fa_fwd_varlen(None, None) == NULL
+    assert fb.lib().fa_fwd_varlen(ctypes.byref(good_varlen(total_q=0, max_seqlen_q=0)), None) == OK
+    assert fb.lib().fa_fwd_varlen(ctypes.byref(good_varlen(max_seqlen_q=0)), None) == OK
+
+
+def good_paged(**kw):
+    a = fb.DecodePagedArgs(q=FAKE, k_pages=FAKE, v_pages=FAKE, block_table=FAKE, seq_lens=FAKE,
+                           o=FAKE, lse=FAKE, q_stride=fb.c_i64x2(32 * 128, 128),
+                           k_stride=fb.c_i64x3(8 * 16 * 128, 16 * 128, 128),
+                           v_stride=fb.c_i64x3(8 * 16 * 128, 16 * 128, 128),
+                           o_stride=fb.c_i64x2(32 * 128, 128), table_stride=256,
+                           Bs=4, Hq=32, Hkv=8, D=128, num_pages=1024, page_size=16,
+                           max_pages_per_seq=256, max_len=4096, split_len=2048,
+                           in_dtype=fb.FA_BF16, out_dtype=fb.FA_BF16, scale=0.088)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+PAGED_BAD = [
+    ({"page_size": 8}, SHAPE), ({"page_size": 48}, SHAPE), ({"page_size": 0}, SHAPE),
+    ({"max_len": 4097}, SHAPE), ({"table_stride": 255}, SHAPE), ({"num_pages": -1}, SHAPE),
+    ({"split_len": 1000}, SHAPE), ({"Hq": 30}, SHAPE), ({"D": 80}, UNSUP),
+    ({"in_dtype": fb.FA_F32}, DTYPE), ({"scale": float("nan")}, ARG),
+    ({"block_table": None}, NULL), ({"seq_lens": None}, NULL), ({"v_pages": None}, NULL),
+    ({"block_table": FAKE + 2}, STRIDE), ({"k_pages": FAKE + 4}, STRIDE),
+    ({"page_size": 1 << 20, "max_pages_per_seq": 1, "table_stride": 1,
+      "k_stride": fb.c_i64x3(1 << 30, 1 << 7, 8 * 128)}, SHAPE),
+]
+
+
+@pytest.mark.parametrize("change,status", PAGED_BAD)
+def test_decode_paged_rejects_bad_arguments(change, status):
+    a = good_paged(**change)
+    assert fb.lib().fa_decode_paged(ctypes.byref(a), FAKE, 1 << 30, None) == status
+    assert fb.lib().fa_decode_paged_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def test_decode_paged_workspace_query():
+    a = good_paged(Bs=64)
+    need = fb.lib().fa_decode_paged_workspace_bytes(ctypes.byref(a))
+    rows = 64 * 32 * 2
+    assert need == rows * 128 * 4 + rows * 4
+    assert fb.lib().fa_decode_paged(ctypes.byref(a), FAKE, need - 1, None) == WS
+    assert fb.lib().fa_decode_paged(ctypes.byref(good_paged(Bs=0)), None, 0, None) == OK

@@ -11,23 +11,12 @@ import torch
 import io_aware_tiled_10_amd as fa
 import oracle
 from io_aware_tiled_10_amd import inputs
-from tests.helpers import DEV, assert_fwd_close, say, to_host
+from tests.helpers import DEV, assert_fwd_close, dense_cache_on_device, say, to_host
 
 pytestmark = pytest.mark.gpu
 
 
-def build_cache(d: inputs.DecodeInputs, lmax: int):
-    bs = len(d.seq_lens)
-    kc = torch.full((bs, d.Hkv, lmax, d.D), float("nan"), dtype=torch.bfloat16, device=DEV)
-    vc = torch.full_like(kc, float("nan"))
-    for s in range(bs):
-        L = int(d.seq_lens[s])
-        if L == 0:
-            continue
-        kb, vb = d.kv_bits(s)
-        kc[s, :, :L] = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(DEV)
-        vc[s, :, :L] = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(DEV)
-    return kc, vc
+build_cache = dense_cache_on_device
 
 
 def oracle_decode(d: inputs.DecodeInputs, seqs):
