@@ -14,6 +14,11 @@ inputs already resident in HBM:
   decode  split-KV decode, 64 sequences x 1 token, Hq32 Hkv8 D128, bf16 cache,
           lengths U[1024, 32768] (seed 0), chunks of 2048 + merge
 
+--aux also times, outside the step: the B4 H16 N2048 D128 forwards (non-causal and
+causal), a packed variable-length causal forward (32 sequences of U[256, 4096] rows,
+Hq32 Hkv8 D128) and the decode workload read from page pools of 16 and of 256 rows
+in random page order through a block table.
+
 Throughput counts only matmul FLOPs over the (query, key) pairs that exist:
 4*D per pair for the forward and the decode (QK^T and PV), 10*D per pair for the
 backward (five products, one of them the recompute of S).  Decode bandwidth counts
@@ -57,6 +62,10 @@ BWD_CFG = dict(B=2, H=16, N=4096, D=128, causal=True)
 DEC_CFG = dict(Bs=64, Hq=32, Hkv=8, D=128, lo=1024, hi=32768, split=2048, lmax=32768)
 AUX_CFGS = {"fwd_b4h16n2048_noncausal": dict(B=4, Hq=16, Hkv=16, N=2048, D=128, causal=False),
             "fwd_b4h16n2048_causal": dict(B=4, Hq=16, Hkv=16, N=2048, D=128, causal=True)}
+# packed variable-length prefill: 32 sequences of U[256, 4096] rows (seed 0), causal GQA
+VARLEN_CFG = dict(B=32, lo=256, hi=4096, Hq=32, Hkv=8, D=128, causal=True)
+# the decode workload's cache scattered over pages of 16 and of 256 rows, random page order
+PAGED_SIZES = (16, 256)
 
 CSRC = os.path.join(ROOT, "io_aware_tiled_10_amd", "csrc")
 # sources the forward kernel's machine code depends on
@@ -150,6 +159,61 @@ class DecodeLeg:
     def run(self):
         fa.decode(self.q, self.kc, self.vc, self.sl, max_len=self.cfg["lmax"], split_len=self.cfg["split"],
                   workspace=self.ws, out=self.o, lse_out=self.lse)
+
+
+class DecodePagedLeg:
+    """The decode workload read through a block table from a randomly ordered page pool."""
+
+    def __init__(self, dec: DecodeLeg, page: int, seed=0):
+        self.dec = dec
+        self.kp, self.vp, self.table = inputs.paged_pools_torch(dec.kc, dec.vc, dec.lens, page, seed)
+        self.max_len = int(dec.lens.max())
+        a = fa.binding.decode_paged_args(dec.q, self.kp, self.vp, self.table, dec.sl, dec.o, dec.lse,
+                                         page, self.max_len, dec.cfg["split"], None)
+        import ctypes
+        self.ws = torch.empty(fa.lib().fa_decode_paged_workspace_bytes(ctypes.byref(a)),
+                              dtype=torch.uint8, device=DEV)
+        self.flops = dec.flops
+        # cached K/V once, q, O, LSE, plus the block-table entries that are read
+        self.bytes = dec.bytes + 4 * sum((int(L) + page - 1) // page for L in dec.lens)
+
+    def run(self):
+        d = self.dec
+        fa.decode_paged(d.q, self.kp, self.vp, self.table, d.sl, max_len=self.max_len,
+                        split_len=d.cfg["split"], workspace=self.ws, out=d.o, lse_out=d.lse)
+
+
+class FwdVarlenLeg:
+    """Packed variable-length causal forward (prefill of a ragged batch)."""
+
+    def __init__(self, cfg, seed=0):
+        self.cfg = cfg
+        lens = [int(x) for x in inputs.ragged_lengths(cfg["B"], cfg["lo"], cfg["hi"], seed)]
+        x = inputs.varlen_inputs(lens, lens, cfg["Hq"], cfg["Hkv"], cfg["D"], "bf16", seed)
+        self.q, self.k, self.v = bf16_dev(x.q), bf16_dev(x.k), bf16_dev(x.v)
+        self.cu = torch.from_numpy(x.cu_q).to(DEV)
+        self.max_len = max(lens)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((cfg["Hq"], self.q.shape[0]), dtype=torch.float32, device=DEV)
+        self.flops = 4 * cfg["D"] * cfg["Hq"] * sum(pairs(n, n, cfg["causal"]) for n in lens)
+        self.tokens = sum(lens)
+
+    def run(self):
+        fa.fwd_varlen(self.q, self.k, self.v, self.cu, self.cu, self.max_len, causal=self.cfg["causal"],
+                      out=self.o, lse_out=self.lse)
+
+
+def time_aux(leg, stream, reps=20):
+    for _ in range(3):
+        leg.run()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        leg.run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
 
 
 # ------------------------------------------------------------------------------------
@@ -297,7 +361,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="fwd,bwd,decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--aux", action="store_true", help="also time the B4 H16 N2048 forwards")
+    ap.add_argument("--aux", action="store_true",
+                    help="also time the B4 H16 N2048 forwards, the packed variable-length forward and "
+                         "the paged-cache decode (outside the step)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--ceilings", action="store_true",
@@ -310,7 +376,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the forward shards over heads with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the forward would shard over heads with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -370,21 +436,27 @@ def main():
         out_legs[n] = rec
 
     if args.aux:
+        def flops_rec(leg, ms):
+            tf = leg.flops / (ms * 1e-3) / 1e12
+            return {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                    "in_step": False}
+
         for name, cfg in AUX_CFGS.items():
             leg = FwdLeg(cfg)
-            for _ in range(3):
-                leg.run()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            a.record(stream)
-            for _ in range(20):
-                leg.run()
-            b.record(stream)
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b) / 20
-            tf = leg.flops / (ms * 1e-3) / 1e12
-            out_legs[name] = {"ms": round(ms, 4), "tflops": round(tf, 2),
-                              "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "in_step": False}
+            out_legs[name] = flops_rec(leg, time_aux(leg, stream))
+            del leg
+        leg = FwdVarlenLeg(VARLEN_CFG)
+        out_legs["fwd_varlen_32seqs_u256_4096_causal"] = dict(flops_rec(leg, time_aux(leg, stream)),
+                                                               tokens=leg.tokens)
+        del leg
+        dec = legs["decode"] if "decode" in legs else DecodeLeg(DEC_CFG)
+        for page in PAGED_SIZES:
+            leg = DecodePagedLeg(dec, page)
+            ms = time_aux(leg, stream)
+            gbs = leg.bytes / (ms * 1e-3) / 1e9
+            out_legs[f"decode_paged_p{page}"] = {"ms": round(ms, 4), "hbm_gbs": round(gbs, 1),
+                                                 "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                                                 "algorithmic_bytes": int(leg.bytes), "in_step": False}
             del leg
 
     if args.calib_copy:

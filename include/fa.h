@@ -253,7 +253,8 @@ fa_status fa_fwd_varlen(const fa_fwd_varlen_args *args, void *stream);
  *   page_size  a power of two, 16 .. 2^20
  *   max_pages_per_seq  usable entries per table row: max_len <= max_pages_per_seq *
  *      page_size, table_stride >= max_pages_per_seq
- *   q, seq_lens, o, lse, max_len, split_len, dtypes and scale as in fa_decode.
+ *   split_len  as in fa_decode, at most 4096
+ *   q, seq_lens, o, lse, max_len, dtypes and scale as in fa_decode.
  * Workspace: fa_decode_paged_workspace_bytes() bytes of chunk partials, merged as in
  * fa_decode.  A sequence with L_s = 0 gets O = 0, LSE = -inf.
  * ------------------------------------------------------------------------------- */

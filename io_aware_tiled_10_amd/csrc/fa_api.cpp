@@ -167,7 +167,7 @@ fa_status validate_decode_paged(const fa_decode_paged_args* a) {
   if (a->num_pages < 0 || a->max_pages_per_seq < 0 || a->max_len < 0) return FA_ERR_SHAPE;
   if ((int64_t)a->max_len > (int64_t)a->max_pages_per_seq * a->page_size) return FA_ERR_SHAPE;
   if (a->table_stride < a->max_pages_per_seq) return FA_ERR_SHAPE;
-  if (a->split_len < 128 || a->split_len % 128 != 0) return FA_ERR_SHAPE;
+  if (a->split_len < 128 || a->split_len % 128 != 0 || a->split_len > 4096) return FA_ERR_SHAPE;
   if (a->in_dtype != FA_BF16) return FA_ERR_DTYPE;
   if (a->out_dtype != FA_BF16 && a->out_dtype != FA_F32) return FA_ERR_DTYPE;
   if (a->D != 64 && a->D != 128) return FA_ERR_UNSUPPORTED;

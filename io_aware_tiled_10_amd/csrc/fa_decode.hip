@@ -129,7 +129,30 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecParams p) {
 
   // block n of this wave covers keys [start + 32 (wave + 4 n), +32); past the chunk the
   // descriptor is empty, nothing is read and the stage is filled with zeros
-  auto issue = [&](int n) {
+  // Paged cache: the page ids of block n of this wave (one per 16-row half; both halves
+  // name the same page when pages hold >= 32 rows), read from a register that lane
+  // 2n + h filled from the block table with the q loads; -1 where no row of the chunk
+  // lies.  A chunk gives a wave at most 32 blocks (split_len <= 4096).
+  struct PageIds {
+    int id[2];
+  };
+  int vpage = -1;
+  if constexpr (PAGED) {
+    const int row = start + kDecBlock * (wave + kDecWaves * (lane >> 1)) + 16 * (lane & 1);
+    if (row < end) vpage = p.table[s * p.table_stride + (row >> p.page_shift)];
+  }
+  auto pages_of = [&](int n) {
+    PageIds r{{-1, -1}};
+    if constexpr (PAGED) {
+      if (2 * n + 1 < 64) {
+        r.id[0] = __builtin_amdgcn_readlane(vpage, 2 * n);
+        r.id[1] = __builtin_amdgcn_readlane(vpage, 2 * n + 1);
+      }
+    }
+    return r;
+  };
+
+  auto issue = [&](int n, const PageIds& pid) {
     const int key0 = start + kDecBlock * (wave + kDecWaves * n);
     unsigned char* st = ring + (n & 1) * T::STAGE;
     if constexpr (!PAGED) {
@@ -144,23 +167,17 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecParams p) {
       // The block's 32 rows lie in one page (pages of >= 32 rows) or in two 16-row
       // pages (half h = rows 16h ..).  One descriptor per page spans that page's rows
       // inside the chunk, so rows past the chunk read as zeros, and so does a page whose
-      // id is outside the pool; no table entry is read for a block past the chunk.  A
-      // DMA instruction's RPI rows never straddle a page (RPI <= 16 <= page size).
+      // id is outside the pool.  A DMA instruction's RPI rows never straddle a page
+      // (RPI <= 16 <= page size).
       const int psz = 1 << p.page_shift;
-      const bool two = p.page_shift == 4;
       __amdgpu_buffer_rsrc_t rk[2], rv[2];
       int pstart[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        if (h == 1 && !two) {
-          rk[1] = rk[0], rv[1] = rv[0], pstart[1] = pstart[0];
-          break;
-        }
         const int row = key0 + 16 * h;
         pstart[h] = row & ~(psz - 1);
         int valid = min(end - pstart[h], psz);
-        int page = 0;
-        if (row < end) page = p.table[s * p.table_stride + (row >> p.page_shift)];
+        int page = pid.id[h];
         if (row >= end || page < 0 || page >= p.num_pages) valid = 0, page = 0;
         rk[h] = make_rsrc(kb + (int64_t)page * p.ks0, rows_span(valid, kpitch, T::ROWB));
         rv[h] = make_rsrc(vb + (int64_t)page * p.vs0, rows_span(valid, vpitch, T::ROWB));
@@ -185,9 +202,10 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecParams p) {
 
   const int mine = wave < nb ? (nb - wave + kDecWaves - 1) / kDecWaves : 0;
   if (mine > 0) {
-    issue(0);
-    issue(1);
+    issue(0, pages_of(0));
+    issue(1, pages_of(1));
     for (int n = 0; n < mine; ++n) {
+      const PageIds next = pages_of(n + 2);
       // block n landed; the 2 * NDMA loads of block n + 1 may still be in flight
       if constexpr (T::NDMA == 8) FA_WAIT_VMCNT(16); else FA_WAIT_VMCNT(8);
       static_assert(T::NDMA == 8 || T::NDMA == 4, "wait count below assumes D = 128 or 64");
@@ -246,7 +264,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecParams p) {
                           pf[ts], acc[d]);
       }
       FA_WAIT_LGKMCNT0();  // every read of this stage has returned
-      issue(n + 2);
+      issue(n + 2, next);
     }
     FA_WAIT_VMCNT(0);  // the trailing (empty) loads write the ring too
   }

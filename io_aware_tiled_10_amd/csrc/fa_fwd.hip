@@ -94,14 +94,17 @@ fwd_bf16_kernel(FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // ---- which tile: XCD-contiguous, KV-head-major, heavy causal tiles first
+  // ---- which tile: XCD-contiguous, heavy causal tiles first.  The tiles of one (batch
+  // entry, KV head) are consecutive, so they share an XCD's L2; the KV head varies
+  // slowest, so every XCD receives every batch entry and sequences of different length
+  // (packed batches) spread evenly over the XCDs.
   int t = xcd_contiguous(blockIdx.x, gridDim.x);
   const int gi = t % p.G;
   t /= p.G;
   const int rank = t % p.nqt;
   t /= p.nqt;
-  const int hkv = t % p.Hkv;
-  const int b = t / p.Hkv;
+  const int b = t % p.B;
+  const int hkv = t / p.B;
   const int qt = p.causal ? p.nqt - 1 - rank : rank;
   const int hq = hkv * p.G + gi;
 

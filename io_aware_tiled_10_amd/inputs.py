@@ -1,11 +1,11 @@
-"""Seeded synthetic inputs for the attention workloads (numpy only).
+"""Seeded synthetic inputs for the attention workloads.
 
 This module holds no attention arithmetic.  It draws i.i.d. N(0, 1) values with
 numpy's PCG64 generator and rounds them to bf16 (round to nearest, ties to
 even) where a workload is bf16, so that the HIP library and the fp64 oracle are
 handed exactly the same numbers.
 
-Recipe (stated once more in the design doc):
+Recipe:
 
 * forward / backward: ``rng = default_rng(seed)``; draw q, k, v (then dO for
   the backward) in that order, each ``rng.standard_normal(shape, float32)`` in
@@ -14,7 +14,13 @@ Recipe (stated once more in the design doc):
   ``rng.integers(lo, hi, endpoint=True, size=Bs)`` first, then q [Bs, Hq, D];
   the cached keys and values of sequence s come from their own generator
   ``default_rng([seed, 1, s])`` (k then v, each [Hkv, L_s, D]) so that a single
-  sequence can be regenerated without drawing the whole cache.
+  sequence can be regenerated without drawing the whole cache;
+* packed variable-length batches: lengths ``default_rng([seed, 7]).integers(lo,
+  hi, endpoint=True)``; q, k, v drawn from ``default_rng([seed, 5])`` in that
+  order as [total rows, H, D];
+* paged caches: the decode cache's pages are placed in the order of
+  ``default_rng([seed, 9])`` (numpy pools) or ``default_rng([seed, 11])`` (torch
+  pools) permutations of the page pool; unused rows hold NaN.
 """
 
 from __future__ import annotations
@@ -176,3 +182,42 @@ def paged_cache(dec: DecodeInputs, page_size: int, seed: int = 0, spare_pages: i
             kp[page, :, :n] = k[:, j * page_size:j * page_size + n]
             vp[page, :, :n] = v[:, j * page_size:j * page_size + n]
     return PagedCache(kp, vp, table, page_size)
+
+
+def paged_pools_torch(kc, vc, lens, page_size: int, seed: int = 0, spare: int = 0,
+                      row_major_heads: bool = False):
+    """Scatter dense [Bs, Hkv, Lmax, D] caches (torch, any device) into page pools.
+
+    Pages are placed in a seeded random order.  Returns (k_pages, v_pages, block_table):
+    pools indexed [page, head, row, D] -- contiguous, or with ``row_major_heads`` views
+    of [page, row, head, D] storage -- whose rows past a sequence's length, and whose
+    spare pages, hold NaN; table entries (int32) past a sequence hold -1.
+    """
+    import torch
+
+    dev = kc.device
+    bs, hkv, lmax, d = kc.shape
+    npg = [(int(L) + page_size - 1) // page_size for L in lens]
+    total = sum(npg) + spare
+    perm = torch.from_numpy(np.random.default_rng([seed, 11]).permutation(total)).to(dev)
+    table = torch.full((bs, max(npg + [1])), -1, dtype=torch.int32, device=dev)
+    s_idx = torch.from_numpy(np.repeat(np.arange(bs), npg)).to(dev)
+    j_idx = torch.from_numpy(np.concatenate([np.arange(n) for n in npg] + [np.zeros(0, np.int64)])).to(dev)
+    used = perm[:len(s_idx)]
+    pos = j_idx[:, None] * page_size + torch.arange(page_size, device=dev)[None, :]
+    lens_t = torch.tensor([int(L) for L in lens], dtype=torch.long, device=dev)
+    inside = pos < lens_t[s_idx][:, None]
+    pos = pos.clamp(max=lmax - 1)
+    if len(s_idx):
+        table[s_idx, j_idx] = used.to(torch.int32)
+    pools = []
+    for c in (kc, vc):
+        pool = torch.full((total, page_size, hkv, d), float("nan"), dtype=c.dtype, device=dev)
+        cr = c.permute(0, 2, 1, 3)
+        for p0 in range(0, len(s_idx), 4096):  # bounded temporaries
+            sl = slice(p0, p0 + 4096)
+            rows = cr[s_idx[sl][:, None], pos[sl]]  # [pages, page_size, Hkv, D]
+            rows[~inside[sl]] = float("nan")
+            pool[used[sl]] = rows
+        pools.append(pool.transpose(1, 2) if row_major_heads else pool.transpose(1, 2).contiguous())
+    return pools[0], pools[1], table

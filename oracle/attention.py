@@ -28,7 +28,7 @@ Sources (the four web pages the method is described on):
   the two-block derivation) and section 四 (deferred normalisation, recompute
   from the saved m and l, GQA).
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 
 * The log-sum-exp saved for the backward is LSE = m + ln(l), natural log, in the
   units of the scaled scores.

@@ -5,6 +5,8 @@ import sys
 import numpy as np
 import torch
 
+from io_aware_tiled_10_amd import inputs
+
 DEV = "cuda:0"
 
 
@@ -70,33 +72,5 @@ def dense_cache_on_device(d, lmax: int):
 
 def paged_pools(kc: torch.Tensor, vc: torch.Tensor, lens, page_size: int, seed: int,
                 spare: int = 0, row_major_heads: bool = False):
-    """Scatter dense [Bs, Hkv, Lmax, D] caches into page pools in a seeded random order.
-
-    Returns (k_pages, v_pages, block_table): pools indexed [page, head, row, D] --
-    contiguous, or with ``row_major_heads`` views of [page, row, head, D] storage --
-    whose rows past a sequence's length, and whose spare pages, hold NaN; table
-    entries past a sequence hold -1.  Data movement only.
-    """
-    bs, hkv, lmax, d = kc.shape
-    npg = [(int(L) + page_size - 1) // page_size for L in lens]
-    total = sum(npg) + spare
-    perm = torch.from_numpy(np.random.default_rng([seed, 11]).permutation(total)).to(DEV)
-    table = torch.full((bs, max(npg + [1])), -1, dtype=torch.int32, device=DEV)
-    s_idx = torch.tensor([s for s in range(bs) for _ in range(npg[s])], dtype=torch.long, device=DEV)
-    j_idx = torch.tensor([j for s in range(bs) for j in range(npg[s])], dtype=torch.long, device=DEV)
-    used = perm[:len(s_idx)]
-    pos = j_idx[:, None] * page_size + torch.arange(page_size, device=DEV)[None, :]
-    lens_t = torch.tensor([int(L) for L in lens], dtype=torch.long, device=DEV)
-    inside = pos < lens_t[s_idx][:, None]
-    pos = pos.clamp(max=lmax - 1)
-    if len(s_idx):
-        table[s_idx, j_idx] = used.to(torch.int32)
-    pools = []
-    for c in (kc, vc):
-        pool = torch.full((total, page_size, hkv, d), float("nan"), dtype=c.dtype, device=DEV)
-        if len(s_idx):
-            rows = c.permute(0, 2, 1, 3)[s_idx[:, None], pos]  # [pages, page_size, Hkv, D]
-            rows[~inside] = float("nan")
-            pool[used] = rows
-        pools.append(pool.transpose(1, 2) if row_major_heads else pool.transpose(1, 2).contiguous())
-    return pools[0], pools[1], table
+    """Page pools and block table holding kc / vc (inputs.paged_pools_torch)."""
+    return inputs.paged_pools_torch(kc, vc, lens, page_size, seed, spare, row_major_heads)

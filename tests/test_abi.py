@@ -209,7 +209,7 @@ def good_paged(**kw):
 PAGED_BAD = [
     ({"page_size": 8}, SHAPE), ({"page_size": 48}, SHAPE), ({"page_size": 0}, SHAPE),
     ({"max_len": 4097}, SHAPE), ({"table_stride": 255}, SHAPE), ({"num_pages": -1}, SHAPE),
-    ({"split_len": 1000}, SHAPE), ({"Hq": 30}, SHAPE), ({"D": 80}, UNSUP),
+    ({"split_len": 1000}, SHAPE), ({"split_len": 8192}, SHAPE), ({"Hq": 30}, SHAPE), ({"D": 80}, UNSUP),
     ({"in_dtype": fb.FA_F32}, DTYPE), ({"scale": float("nan")}, ARG),
     ({"block_table": None}, NULL), ({"seq_lens": None}, NULL), ({"v_pages": None}, NULL),
     ({"block_table": FAKE + 2}, STRIDE), ({"k_pages": FAKE + 4}, STRIDE),
