@@ -15,7 +15,7 @@ inputs already resident in HBM:
           lengths U[1024, 32768] (seed 0), chunks of 2048 + merge
 
 --aux also times, outside the step: the B4 H16 N2048 D128 forwards (non-causal and
-causal), a packed variable-length causal forward (32 sequences of U[256, 4096] rows,
+causal), the GQA backward at B1 Hq32 Hkv8 N16384 D128 causal, a packed variable-length causal forward (32 sequences of U[256, 4096] rows,
 Hq32 Hkv8 D128) and the decode workload read from page pools of 16 and of 256 rows
 in random page order through a block table.
 
@@ -64,6 +64,8 @@ AUX_CFGS = {"fwd_b4h16n2048_noncausal": dict(B=4, Hq=16, Hkv=16, N=2048, D=128, 
             "fwd_b4h16n2048_causal": dict(B=4, Hq=16, Hkv=16, N=2048, D=128, causal=True)}
 # packed variable-length prefill: 32 sequences of U[256, 4096] rows (seed 0), causal GQA
 VARLEN_CFG = dict(B=32, lo=256, hi=4096, Hq=32, Hkv=8, D=128, causal=True)
+# GQA backward at the long-sequence forward's shape
+BWD_GQA_CFG = dict(B=1, Hq=32, Hkv=8, N=16384, D=128, causal=True)
 # the decode workload's cache scattered over pages of 16 and of 256 rows, random page order
 PAGED_SIZES = (16, 256)
 
@@ -110,8 +112,9 @@ class FwdLeg:
 class BwdLeg:
     def __init__(self, cfg, seed=0):
         self.cfg = cfg
-        B, H, N, D = cfg["B"], cfg["H"], cfg["N"], cfg["D"]
-        x = inputs.attention_inputs(B, H, H, N, N, D, "bf16", seed, with_grad=True)
+        B, H, N, D = cfg["B"], cfg.get("Hq", cfg.get("H")), cfg["N"], cfg["D"]
+        Hkv = cfg.get("Hkv", H)
+        x = inputs.attention_inputs(B, H, Hkv, N, N, D, "bf16", seed, with_grad=True)
         self.q, self.k, self.v, self.do = bf16_dev(x.q), bf16_dev(x.k), bf16_dev(x.v), bf16_dev(x.do)
         self.o, self.lse = fa.fwd(self.q, self.k, self.v, causal=cfg["causal"])
         self.grads = (torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v))
@@ -445,6 +448,9 @@ def main():
             leg = FwdLeg(cfg)
             out_legs[name] = flops_rec(leg, time_aux(leg, stream))
             del leg
+        leg = BwdLeg(BWD_GQA_CFG)
+        out_legs["bwd_gqa_b1h32kv8n16384_causal"] = flops_rec(leg, time_aux(leg, stream, reps=5))
+        del leg
         leg = FwdVarlenLeg(VARLEN_CFG)
         out_legs["fwd_varlen_32seqs_u256_4096_causal"] = dict(flops_rec(leg, time_aux(leg, stream)),
                                                                tokens=leg.tokens)

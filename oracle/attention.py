@@ -58,6 +58,7 @@ __all__ = [
     "visible_mask",
     "attn_fwd",
     "attn_bwd",
+    "attn_bwd_dq_rows",
     "attn_decode",
     "attn_fwd_varlen",
     "attn_decode_paged",
@@ -213,6 +214,35 @@ def attn_bwd(q, k, v, do, scale: Optional[float] = None, causal: bool = False,
                 lse[b, h, rr] = l_
                 delta[b, h, rr] = di
     return dq, dk, dv, o, lse, delta
+
+
+def attn_bwd_dq_rows(q, k, v, do, rows: Sequence[int], scale: Optional[float] = None,
+                     causal: bool = False, kv_lens: Optional[Sequence[int]] = None) -> np.ndarray:
+    """dQ of the query rows in ``rows`` only, by the relations of ``attn_bwd``.
+
+    A row's dQ needs its own rows of S, P, O and dP and nothing from the other
+    query rows, so sampled rows of a large problem are computed exactly without
+    the rest.  Returns dq [B, Hq, len(rows), D] in float64.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    b_, hq_, nq, d = q.shape
+    _, hkv, nk, _ = k.shape
+    g = hq_ // hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rr = np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((b_, hq_, len(rr), d))
+    for b in range(b_):
+        lk = _kv_len_of(kv_lens, b, nk)
+        for h in range(hq_):
+            kh, vh = k[b, h // g, :lk], v[b, h // g, :lk]
+            s = scale * (q[b, h, rr] @ kh.T)
+            p, _ = _softmax_rows(s, visible_mask(rr, nq, lk, lk, causal))
+            doh = do[b, h, rr]
+            di = np.sum(doh * (p @ vh), axis=-1)
+            ds = p * (doh @ vh.T - di[:, None])
+            dq[b, h] = scale * (ds @ kh)
+    return dq
 
 
 def attn_decode(q, k_cache, v_cache, seq_lens: Sequence[int],

@@ -86,3 +86,37 @@ def test_bwd_is_deterministic():
     torch.cuda.synchronize()
     for x1, x2 in zip(a, b):
         assert torch.equal(x1, x2)
+
+
+def test_bwd_gqa_full_size_c3_shape():
+    # B1 Hq32 Hkv8 N16384 D128 causal: sampled dQ rows against the oracle; dK and dV
+    # against the MHA backward with every KV head repeated for its 4 query heads,
+    # summed over the group (the MHA path is checked against the oracle above)
+    say("bwd GQA full c3 shape")
+    B, Hq, Hkv, N, D = 1, 32, 8, 16384, 128
+    x = inputs.attention_inputs(B, Hq, Hkv, N, N, D, "bf16", seed=0, with_grad=True)
+    q, k, v, do = to_dev(x.q), to_dev(x.k), to_dev(x.v), to_dev(x.do)
+    o, lse = fa.fwd(q, k, v, causal=True)
+    dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=True)
+    kr = k.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+    vr = v.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+    o2, lse2 = fa.fwd(q, kr, vr, causal=True)
+    _, dk2, dv2 = fa.bwd(q, kr, vr, o2, do, lse2, causal=True)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    dk_sum = dk2.float().view(B, Hkv, Hq // Hkv, N, D).sum(2)
+    dv_sum = dv2.float().view(B, Hkv, Hq // Hkv, N, D).sum(2)
+    for nm, g, r in (("dk", dk, dk_sum), ("dv", dv, dv_sum)):
+        e = rel_l2(to_host(g), to_host(r))
+        say(f"  {nm} vs summed MHA rel-L2 {e:.3e}")
+        assert e <= 1e-2, (nm, e)
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, N - 1], rng.integers(0, N, 11)]))
+    for h in (0, 13, 31):
+        g = h // (Hq // Hkv)
+        ref = oracle.attn_bwd_dq_rows(x.q[:, h:h + 1], x.k[:, g:g + 1], x.v[:, g:g + 1], x.do[:, h:h + 1],
+                                      rows, None, True)
+        e = rel_l2(to_host(dq[:, h:h + 1, rows]), ref)
+        say(f"  h{h} sampled dq rel-L2 {e:.3e}")
+        assert e <= 2e-2, (h, e)

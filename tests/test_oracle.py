@@ -468,3 +468,14 @@ def test_planted_backward_sign_mistake_is_caught_by_finite_differences():
                          - np.sum(do * oracle.attn_fwd(qm, k, v, 1.0)[0])) / (2 * h)
     assert np.abs(num - dq[0, 0]).max() < 1e-7
     assert np.abs(num - dq_bad).max() > 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_dq_rows_equal_the_full_backward(causal):
+    # attn_bwd is pinned by central finite differences; the sampled-row form must agree
+    rng = np.random.default_rng(31)
+    q, k, v, do = (rng.standard_normal(s) for s in ((2, 4, 37, 16), (2, 2, 45, 16), (2, 2, 45, 16), (2, 4, 37, 16)))
+    full = ora.attn_bwd(q, k, v, do, None, causal, [45, 20])[0]
+    rows = [0, 5, 36, 17]
+    part = ora.attn_bwd_dq_rows(q, k, v, do, rows, None, causal, [45, 20])
+    np.testing.assert_allclose(part, full[:, :, rows], rtol=0, atol=1e-12)
