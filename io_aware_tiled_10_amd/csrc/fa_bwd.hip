@@ -29,6 +29,8 @@
 //     Recomputing S and dP here costs two more products per (query, key) pair than
 //     accumulating dQ inside bwd_kv, but removes the device-scope fp32 atomics, which
 //     on a multi-XCD part are executed beyond the per-XCD L2.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -256,29 +258,37 @@ bwd_kv_kernel(BwdParams p) {
       }
     }
 
-    // (2) P = exp(S - LSE), dS = P (dP - D_i); zero where the pair does not exist
+    // (2) P = exp(S - LSE), dS = P (dP - D_i); zero where the pair does not exist.  Two
+    //     instances: tiles that cross no edge run without any per-element test.
     const bool edge = (k0 + BC > lk) || (q0 + BR > p.Nq) || (p.causal && k0 + BC - 1 > q0 + diag);
+    auto probs = [&](auto masked) {
+      constexpr bool M = decltype(masked)::value;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int ql = 32 * qb + 8 * rg + 4 * hi;
-        const f32x4_t st01 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql);
-        const f32x4_t st23 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql + 4);
-        const float l2[4] = {st01[0], st01[2], st23[0], st23[2]};
-        const float dd[4] = {st01[1], st01[3], st23[1], st23[3]};
+        for (int rg = 0; rg < 4; ++rg) {
+          const int ql = 32 * qb + 8 * rg + 4 * hi;
+          const f32x4_t st01 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql);
+          const f32x4_t st23 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql + 4);
+          const float l2[4] = {st01[0], st01[2], st23[0], st23[2]};
+          const float dd[4] = {st01[1], st01[3], st23[1], st23[3]};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pv = fast_exp2(fmaf(s[qb][4 * rg + e], c, -l2[e]));
-          if (edge) {
-            const int q = q0 + ql + e;
-            const bool vis = kw < lk && q < p.Nq && (!p.causal || kw <= q + diag);
-            pv = vis ? pv : 0.f;
+          for (int e = 0; e < 4; ++e) {
+            float pv = fast_exp2(fmaf(s[qb][4 * rg + e], c, -l2[e]));
+            if constexpr (M) {
+              const int q = q0 + ql + e;
+              const int lastk = min(lk - 1, p.causal ? q + diag : lk - 1);  // last key q sees
+              pv = ((q < p.Nq) & (kw <= lastk)) ? pv : 0.f;
+            }
+            s[qb][4 * rg + e] = pv;
+            dp[qb][4 * rg + e] = pv * (dp[qb][4 * rg + e] - dd[e]);
           }
-          s[qb][4 * rg + e] = pv;
-          dp[qb][4 * rg + e] = pv * (dp[qb][4 * rg + e] - dd[e]);
         }
-      }
+    };
+    if (edge)
+      probs(std::true_type{});
+    else
+      probs(std::false_type{});
     // P^T and dS^T as A operands: rows = keys, k-elements = queries in register order
     u32x4_t pa[2][2], da[2][2];
 #pragma unroll
