@@ -47,10 +47,18 @@ constexpr int kBwdSlots = 3;            // ring depth
 // rows read at one logical slot hit 16 different slots, and 8 consecutive rows read over
 // an aligned group of 4 logical slots (transposing reads) cover every slot exactly twice.
 template <int ROWB>
-__device__ __forceinline__ int swz_rows(int r) {
+__host__ __device__ constexpr int swz_rows(int r) {
   constexpr int RPB = 256 / ROWB, SPR = ROWB / 16;
   const int a = r / RPB;
   return 4 * (a % (SPR / 4)) + (a / (SPR / 4)) % 4;
+}
+// The transposing reads address rows 16 ts + 8 r + v (v < 8) with the swizzle of row
+// 8 r + v and step ts by an immediate: true when the swizzle repeats every 16 rows.
+template <int ROWB>
+constexpr bool swz_period_ok() {
+  for (int r = 0; r < 64; ++r)
+    if (swz_rows<ROWB>(r) != swz_rows<ROWB>(r % 16)) return false;
+  return true;
 }
 
 template <int D>
@@ -69,7 +77,7 @@ struct BwdTile {
   static constexpr int KVBYTES = 2 * kBwdBC * ROWB;       // K and V tiles (set-up only)
   static constexpr int LDS_BYTES = RING > KVBYTES ? RING : KVBYTES;
   static_assert(NDMA * 1024 * kBwdWaves == QBYTES, "a tile must split evenly over the waves");
-  static __device__ __forceinline__ int swz(int r) { return swz_rows<ROWB>(r); }
+  static __host__ __device__ constexpr int swz(int r) { return swz_rows<ROWB>(r); }
 };
 
 // Per query row: stats = (LSE * log2 e, D_i = sum_d dO_id O_id).  Rows whose LSE is -inf
@@ -225,6 +233,15 @@ bwd_kv_kernel(BwdParams p) {
 
   const int qsw = T::swz(l32);  // plain reads of query rows 32 qb + l32
   const uint32_t ring_addr = lds_addr(ring);
+  // transposing reads of slot 0: rows 8 r + vrow (+ 16 ts, an immediate: the row's
+  // swizzle does not depend on ts), 32-column block blk
+  uint32_t trb[2][T::DB];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int blk = 0; blk < T::DB; ++blk)
+      trb[r][blk] = ring_addr + tr_off(T::ROWB, r, blk, T::swz(8 * r + vrow));
+  static_assert(swz_period_ok<T::ROWB>(), "transposing-read swizzle must repeat every 16 rows");
   const float c = p.scale_log2;
 
   if (iters > 0) {
@@ -234,9 +251,11 @@ bwd_kv_kernel(BwdParams p) {
     FA_BARRIER();
   }
 
-  for (int it = 0; it < iters; ++it) {
-    const int slot = it % NS;
-    issue(it + 2, (it + 2) % NS);
+  // One query tile; `slot_c` is it % NS as a compile-time constant, so every LDS
+  // operand address is a per-lane register plus an immediate offset.
+  auto tile = [&](int it, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    issue(it + 2, (slot + 2) % NS);
     const int qt = nqt - 1 - it / p.G;
     const int q0 = qt * BR;
     const unsigned char* qs = ring + slot * T::SLOT;
@@ -306,17 +325,20 @@ bwd_kv_kernel(BwdParams p) {
 #pragma unroll
     for (int d0 = 0; d0 < T::DB; d0 += 2) {
       u32x2_t o[2][4][2], q[2][4][2];
+      // the slot offset goes into the instruction's 16-bit immediate where it fits
+      constexpr int TS = 16 * T::ROWB;  // k-step ts: 16 query rows further
+      constexpr bool kImm = slot * T::SLOT + 3 * TS + T::QBYTES < 65536;
+      constexpr int SO = kImm ? slot * T::SLOT : 0;
 #pragma unroll
       for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
-        for (int ts = 0; ts < 4; ++ts)
-#pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            const int row = 16 * ts + 8 * r + vrow;
-            const uint32_t off = ring_addr + slot * T::SLOT + 16 * ts * T::ROWB +
-                                 tr_off(T::ROWB, r, d0 + dd, T::swz(row));
-            lds_read_tr16x2<0, T::QBYTES>(q[dd][ts][r], o[dd][ts][r], off);
-          }
+        for (int r = 0; r < 2; ++r) {
+          const uint32_t a = trb[r][d0 + dd] + (kImm ? 0u : (uint32_t)(slot * T::SLOT));
+          lds_read_tr16x2<SO, SO + T::QBYTES>(q[dd][0][r], o[dd][0][r], a);
+          lds_read_tr16x2<SO + TS, SO + TS + T::QBYTES>(q[dd][1][r], o[dd][1][r], a);
+          lds_read_tr16x2<SO + 2 * TS, SO + 2 * TS + T::QBYTES>(q[dd][2][r], o[dd][2][r], a);
+          lds_read_tr16x2<SO + 3 * TS, SO + 3 * TS + T::QBYTES>(q[dd][3][r], o[dd][3][r], a);
+        }
 #pragma unroll
       for (int dd = 0; dd < 2; ++dd) {
         lds_wait_tr(o[dd][0][0], o[dd][0][1], o[dd][1][0], o[dd][1][1]);
@@ -339,7 +361,16 @@ bwd_kv_kernel(BwdParams p) {
     wait_ring();         // tile it + 1 has landed (only tile it + 2 may be in flight)
     FA_WAIT_LGKMCNT0();  // this wave's ring reads are done
     FA_BARRIER();
+  };
+  static_assert(NS == 3, "the loop below walks three slots");
+  int it = 0;
+  for (; it + 2 < iters; it += 3) {
+    tile(it, std::integral_constant<int, 0>{});
+    tile(it + 1, std::integral_constant<int, 1>{});
+    tile(it + 2, std::integral_constant<int, 2>{});
   }
+  if (it < iters) tile(it, std::integral_constant<int, 0>{});
+  if (it + 1 < iters) tile(it + 1, std::integral_constant<int, 1>{});
 
   // ---- dK = scale * acc, dV = acc, rounded to bf16; rows >= Nk are not stored (rows in
   //      [Lk, Nk) hold zeros).  Column d = 32 blk + l32, register r holds key
