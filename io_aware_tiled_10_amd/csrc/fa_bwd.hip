@@ -532,9 +532,23 @@ bwd_q_kernel(BwdParams p) {
   wait_vmcnt<kInFlight>();
   FA_BARRIER();
 
-  for (int j = 0; j < nblk; ++j) {
-    const int slot = j % NS;
-    dma(j + T::AHEAD, (j + T::AHEAD) % NS);  // into the slot block j - 1 finished with
+  // transposing reads of K in slot 0: rows 8 r + vrow (+ 16 ts and the slot offset as
+  // immediates; the row swizzle repeats every 16 rows), 32-column block d
+  static_assert(swz_period_ok<T::ROWB>(), "transposing-read swizzle must repeat every 16 rows");
+  static_assert((NS - 1) * T::TBYTES + 3 * 16 * T::ROWB < 65536, "slot offsets must fit the immediate");
+  uint32_t ktb[2][T::DB];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int d = 0; d < T::DB; ++d) {
+      const int row = 8 * r + vrow;
+      ktb[r][d] = kring_addr + row * T::ROWB + 16 * ((4 * d + vlo) ^ T::swz(row)) + 8 * (vi & 1);
+    }
+
+  // One block; `slot_c` is j % NS as a compile-time constant.
+  auto block = [&](int j, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    dma(j + T::AHEAD, (slot + T::AHEAD) % NS);  // into the slot block j - 1 finished with
     const unsigned char* ks = kring + slot * T::TBYTES;
     const unsigned char* vs = vring + slot * T::TBYTES;
 
@@ -561,37 +575,43 @@ bwd_q_kernel(BwdParams p) {
     const bool edge = (key0 + BC > lk) || (p.causal && key0 + BC - 1 > q_wg0 + diag);
     const int last = p.causal ? min(lk - 1, qi + diag) : lk - 1;
     u32x4_t pf[4];
+    auto grads = [&](auto masked) {  // two instances: blocks crossing no edge test nothing
+      constexpr bool M = decltype(masked)::value;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float v2[2];
+        for (int r = 0; r < 16; r += 2) {
+          float v2[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float pv = fast_exp2(fmaf(s[h][r + e], c, -l2));
-          float ds = pv * (dp[h][r + e] - dd);
-          if (edge) {
-            const int key = key0 + 32 * h + 8 * ((r + e) >> 2) + 4 * hi + ((r + e) & 3);
-            ds = key > last ? 0.f : ds;
+          for (int e = 0; e < 2; ++e) {
+            const float pv = fast_exp2(fmaf(s[h][r + e], c, -l2));
+            float ds = pv * (dp[h][r + e] - dd);
+            if constexpr (M) {
+              const int key = key0 + 32 * h + 8 * ((r + e) >> 2) + 4 * hi + ((r + e) & 3);
+              ds = key > last ? 0.f : ds;
+            }
+            v2[e] = ds;
           }
-          v2[e] = ds;
+          pf[2 * h + (r >> 3)][(r & 7) >> 1] = pack_bf16(v2[0], v2[1]);
         }
-        pf[2 * h + (r >> 3)][(r & 7) >> 1] = pack_bf16(v2[0], v2[1]);
-      }
+    };
+    if (edge)
+      grads(std::true_type{});
+    else
+      grads(std::false_type{});
 
     // dQ^T += K^T dS^T; K^T fragments from transposing reads of the K block
 #pragma unroll
     for (int d = 0; d < T::DB; ++d) {
       u32x2_t kt[4][2];
+      constexpr int SO = slot * T::TBYTES, TS = 16 * T::ROWB;
 #pragma unroll
-      for (int ts = 0; ts < 4; ++ts)
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int row = 16 * ts + 8 * r + vrow;
-          const uint32_t off = kring_addr + slot * T::TBYTES + row * T::ROWB +
-                               16 * ((4 * d + vlo) ^ T::swz(row)) + 8 * (vi & 1);
-          lds_read_tr16<0>(kt[ts][r], off);
-        }
+      for (int r = 0; r < 2; ++r) {
+        lds_read_tr16<SO>(kt[0][r], ktb[r][d]);
+        lds_read_tr16<SO + TS>(kt[1][r], ktb[r][d]);
+        lds_read_tr16<SO + 2 * TS>(kt[2][r], ktb[r][d]);
+        lds_read_tr16<SO + 3 * TS>(kt[3][r], ktb[r][d]);
+      }
       lds_wait_tr(kt[0][0], kt[0][1], kt[1][0], kt[1][1]);
       lds_wait_tr(kt[2][0], kt[2][1], kt[3][0], kt[3][1]);
 #pragma unroll
@@ -604,7 +624,14 @@ bwd_q_kernel(BwdParams p) {
     wait_vmcnt<kInFlight>();
     FA_WAIT_LGKMCNT0();
     FA_BARRIER();
+  };
+  static_assert(NS == 2, "the loop below walks two slots");
+  int j = 0;
+  for (; j + 1 < nblk; j += 2) {
+    block(j, std::integral_constant<int, 0>{});
+    block(j + 1, std::integral_constant<int, 1>{});
   }
+  if (j < nblk) block(j, std::integral_constant<int, 0>{});
 
   // ---- dQ = scale * acc (lane = query row, register = head-dim element)
   if (qi < p.Nq) {
