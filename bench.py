@@ -15,7 +15,7 @@ inputs already resident in HBM:
           lengths U[1024, 32768] (seed 0), chunks of 2048 + merge
 
 --aux also times, outside the step: the B4 H16 N2048 D128 forwards (non-causal and
-causal), the GQA backward at B1 Hq32 Hkv8 N16384 D128 causal, a packed variable-length causal forward (32 sequences of U[256, 4096] rows,
+causal), the long forward with E4M3 Q and K (and the quantisation passes), the GQA backward at B1 Hq32 Hkv8 N16384 D128 causal, a packed variable-length causal forward (32 sequences of U[256, 4096] rows,
 Hq32 Hkv8 D128) and the decode workload read from page pools of 16 and of 256 rows
 in random page order through a block table.
 
@@ -162,6 +162,28 @@ class DecodeLeg:
     def run(self):
         fa.decode(self.q, self.kc, self.vc, self.sl, max_len=self.cfg["lmax"], split_len=self.cfg["split"],
                   workspace=self.ws, out=self.o, lse_out=self.lse)
+
+
+class FwdFp8Leg:
+    """The long causal GQA forward with Q and K quantised to E4M3 (per-64-row steps)."""
+
+    def __init__(self, cfg, seed=0):
+        self.cfg = cfg
+        x = inputs.attention_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["N"], cfg["D"], "bf16", seed)
+        self.q, self.k, self.v = bf16_dev(x.q), bf16_dev(x.k), bf16_dev(x.v)
+        self.q8, self.qs = fa.quantize_fp8(self.q)
+        self.k8, self.ks = fa.quantize_fp8(self.k)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:3], dtype=torch.float32, device=DEV)
+        self.flops = 4 * cfg["D"] * pairs(cfg["N"], cfg["N"], cfg["causal"]) * cfg["B"] * cfg["Hq"]
+
+    def run(self):
+        fa.fwd_fp8(self.q8, self.qs, self.k8, self.ks, self.v, causal=self.cfg["causal"], out=self.o,
+                   lse_out=self.lse)
+
+    def quantize(self):
+        fa.quantize_fp8(self.q, out=self.q8, scales_out=self.qs)
+        fa.quantize_fp8(self.k, out=self.k8, scales_out=self.ks)
 
 
 class DecodePagedLeg:
@@ -448,6 +470,14 @@ def main():
             leg = FwdLeg(cfg)
             out_legs[name] = flops_rec(leg, time_aux(leg, stream))
             del leg
+        leg = FwdFp8Leg(FWD_CFG)
+        rec = flops_rec(leg, time_aux(leg, stream))
+
+        class _Q:  # the two quantisation passes for Q and K, timed alone
+            run = leg.quantize
+        rec["quantize_q_k_ms"] = round(time_aux(_Q, stream), 4)
+        out_legs["fwd_fp8qk_b1h32kv8n16384_causal"] = rec
+        del leg
         leg = BwdLeg(BWD_GQA_CFG)
         out_legs["bwd_gqa_b1h32kv8n16384_causal"] = flops_rec(leg, time_aux(leg, stream, reps=5))
         del leg

@@ -19,12 +19,15 @@
  *              partials are merged by the online-softmax update.
  *              Pages: interview answer, 高频追问 2; self-test page, section F.
  *
- * Two variants change only how rows are addressed:
+ * Further variants:
  *
  *   fa_fwd_varlen    the forward over a packed batch of variable-length sequences
  *                    (prefix offsets instead of padding).
  *                    Pages: self-test page, section C (padding masks and variable-length
  *                    sequences).
+ *   fa_quantize_fp8  two-pass E4M3 block quantisation of Q or K (step = block max / 448).
+ *   fa_fwd_fp8       the forward with Q K^T on the E4M3 matrix cores (fp32 accumulation).
+ *                    Pages: V2/V3 article, section FP8低精度 and its formula block.
  *   fa_decode_paged  the split-KV decode over a KV cache kept in fixed-size pages named
  *                    by a per-sequence block table, read page by page where it lies.
  *                    Pages: self-test page, section F (why paged attention or a decode
@@ -282,6 +285,55 @@ typedef struct fa_decode_paged_args {
 size_t fa_decode_paged_workspace_bytes(const fa_decode_paged_args *args);
 fa_status fa_decode_paged(const fa_decode_paged_args *args, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * E4M3 block quantisation (D = 128, block = 64).
+ *   x       [B, H, N, D] bf16 (device), strides in elements
+ *   codes   [B, H, N, D] uint8 (device, written): OCP E4M3 codes of x / Delta, rounded
+ *           to nearest even; strides in bytes
+ *   scales  contiguous [B, H, ceil(N / 64)] fp32 (device, written): Delta of each block of
+ *           64 rows, max|x| / 448 (one fp32 division), 1 for an all-zero block
+ * ------------------------------------------------------------------------------- */
+typedef struct fa_quantize_fp8_args {
+  const void *x;
+  void *codes;
+  float *scales;
+  int64_t x_stride[3];     /* elements: batch, head, row */
+  int64_t codes_stride[3]; /* bytes: batch, head, row */
+  int32_t B, H, N, D;
+  int32_t block;           /* 64 */
+} fa_quantize_fp8_args;
+
+fa_status fa_quantize_fp8(const fa_quantize_fp8_args *args, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Forward with E4M3 Q and K (D = 128).
+ *   q  [B, Hq, Nq, D] E4M3 codes with q_scales contiguous [B, Hq, ceil(Nq / 64)] fp32
+ *   k  [B, Hkv, Nk, D] E4M3 codes with k_scales contiguous [B, Hkv, ceil(Nk / 64)] fp32
+ *      (as written by fa_quantize_fp8; code strides in bytes)
+ *   v  [B, Hkv, Nk, D] bf16; o, lse, kv_lens, scale, causal as in fa_fwd
+ * S = scale * (Delta_q q_hat)(Delta_k k_hat)^T is formed on the E4M3 matrix cores with
+ * fp32 accumulation; the softmax, P (bf16) V and the outputs are those of fa_fwd.
+ * out_dtype FA_BF16 or FA_F32.
+ * ------------------------------------------------------------------------------- */
+typedef struct fa_fwd_fp8_args {
+  const void *q, *k, *v;
+  const float *q_scales, *k_scales;
+  void *o;
+  float *lse;
+  const int32_t *kv_lens;
+  int64_t q_stride[3]; /* bytes: batch, head, seq */
+  int64_t k_stride[3]; /* bytes */
+  int64_t v_stride[3]; /* elements */
+  int64_t o_stride[3]; /* elements */
+  int32_t B, Hq, Hkv, Nq, Nk, D;
+  int32_t block;       /* 64 */
+  int32_t out_dtype;   /* FA_BF16 or FA_F32 */
+  float scale;
+  int32_t causal;
+} fa_fwd_fp8_args;
+
+fa_status fa_fwd_fp8(const fa_fwd_fp8_args *args, void *stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *fa_status_str(int status);

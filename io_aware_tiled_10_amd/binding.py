@@ -90,8 +90,30 @@ class DecodePagedArgs(ctypes.Structure):
     ]
 
 
-EXPORTED = ["fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode",
-            "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
+class QuantizeArgs(ctypes.Structure):
+    _fields_ = [
+        ("x", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+        ("x_stride", c_i64x3), ("codes_stride", c_i64x3),
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+    ]
+
+
+class FwdFp8Args(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("q_scales", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p),
+        ("q_stride", c_i64x3), ("k_stride", c_i64x3), ("v_stride", c_i64x3), ("o_stride", c_i64x3),
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Nq", ctypes.c_int32), ("Nk", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("block", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
+    ]
+
+
+EXPORTED = ["fa_fwd", "fa_fwd_varlen", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd", "fa_bwd_workspace_bytes",
+            "fa_decode", "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
             "fa_status_str", "fa_device_supported", "fa_version"]
 
 _lib = None
@@ -123,6 +145,10 @@ def lib() -> ctypes.CDLL:
         h.fa_decode_paged.restype = ctypes.c_int
         h.fa_decode_paged_workspace_bytes.argtypes = [ctypes.POINTER(DecodePagedArgs)]
         h.fa_decode_paged_workspace_bytes.restype = ctypes.c_size_t
+        h.fa_quantize_fp8.argtypes = [ctypes.POINTER(QuantizeArgs), ctypes.c_void_p]
+        h.fa_quantize_fp8.restype = ctypes.c_int
+        h.fa_fwd_fp8.argtypes = [ctypes.POINTER(FwdFp8Args), ctypes.c_void_p]
+        h.fa_fwd_fp8.restype = ctypes.c_int
         h.fa_status_str.argtypes = [ctypes.c_int]
         h.fa_status_str.restype = ctypes.c_char_p
         h.fa_device_supported.argtypes = [ctypes.c_int]
@@ -227,6 +253,45 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: 
         torch.empty((Hq, Tq), dtype=torch.float32, device=q.device) if with_lse else None)
     a = fwd_varlen_args(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal, scale)
     _check(lib().fa_fwd_varlen(ctypes.byref(a), _stream(q.device)))
+    return o, lse
+
+
+FP8_BLOCK = 64
+
+
+def quantize_fp8(x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 scales_out: Optional[torch.Tensor] = None):
+    """Two-pass E4M3 block quantisation via ``fa_quantize_fp8``.
+
+    x [B, H, N, D] bf16 -> (codes uint8 [B, H, N, D], steps fp32 [B, H, ceil(N / 64)]).
+    """
+    B, H, N, D = x.shape
+    codes = out if out is not None else torch.empty((B, H, N, D), dtype=torch.uint8, device=x.device)
+    nb = (N + FP8_BLOCK - 1) // FP8_BLOCK
+    sc = scales_out if scales_out is not None else torch.empty((B, H, nb), dtype=torch.float32, device=x.device)
+    a = QuantizeArgs(x=_ptr(x), codes=_ptr(codes), scales=_ptr(sc), x_stride=_s3(x), codes_stride=_s3(codes),
+                     B=B, H=H, N=N, D=D, block=FP8_BLOCK)
+    _check(lib().fa_quantize_fp8(ctypes.byref(a), _stream(x.device)))
+    return codes, sc
+
+
+def fwd_fp8(q8: torch.Tensor, q_scales: torch.Tensor, k8: torch.Tensor, k_scales: torch.Tensor,
+            v: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
+            kv_lens: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+            with_lse: bool = True, out: Optional[torch.Tensor] = None,
+            lse_out: Optional[torch.Tensor] = None):
+    """Forward with E4M3 Q and K (codes + per-64-row steps) via ``fa_fwd_fp8``."""
+    B, Hq, Nq, D = q8.shape
+    Hkv, Nk = k8.shape[1], k8.shape[2]
+    o = out if out is not None else torch.empty((B, Hq, Nq, D), dtype=out_dtype, device=q8.device)
+    lse = lse_out if lse_out is not None else (
+        torch.empty((B, Hq, Nq), dtype=torch.float32, device=q8.device) if with_lse else None)
+    a = FwdFp8Args(q=_ptr(q8), k=_ptr(k8), v=_ptr(v), q_scales=_ptr(q_scales), k_scales=_ptr(k_scales),
+                   o=_ptr(o), lse=_ptr(lse), kv_lens=_ptr(kv_lens),
+                   q_stride=_s3(q8), k_stride=_s3(k8), v_stride=_s3(v), o_stride=_s3(o),
+                   B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, D=D, block=FP8_BLOCK, out_dtype=_DT[o.dtype],
+                   scale=_scale(scale, D), causal=int(bool(causal)))
+    _check(lib().fa_fwd_fp8(ctypes.byref(a), _stream(q8.device)))
     return o, lse
 
 

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_quant.hip"]
 
 # The online-softmax kernels take row maxima of MFMA results; without NaN semantics the
 # compiler uses plain v_max/v_max3 instead of canonicalising every input first.  (Inputs

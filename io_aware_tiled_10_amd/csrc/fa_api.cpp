@@ -147,6 +147,43 @@ fa_status validate_decode(const fa_decode_args* a) {
   return FA_OK;
 }
 
+fa_status validate_quantize(const fa_quantize_fp8_args* a) {
+  if (!a) return FA_ERR_NULL_PTR;
+  if (a->B < 1 || a->H < 1 || a->N < 0 || a->D < 1) return FA_ERR_SHAPE;
+  if (a->block != 64) return FA_ERR_UNSUPPORTED;
+  if (a->D != 128) return FA_ERR_UNSUPPORTED;
+  if (a->N == 0) return FA_OK;
+  if (!a->x || !a->codes || !a->scales) return FA_ERR_NULL_PTR;
+  if (!aligned16(a->x) || !aligned16(a->codes)) return FA_ERR_STRIDE;
+  if (reinterpret_cast<uintptr_t>(a->scales) & 3u) return FA_ERR_STRIDE;
+  if (!strides_ok(a->x_stride, 3, 2) || !strides_ok(a->codes_stride, 3, 1)) return FA_ERR_STRIDE;
+  return FA_OK;
+}
+
+fa_status validate_fwd_fp8(const fa_fwd_fp8_args* a) {
+  if (!a) return FA_ERR_NULL_PTR;
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->Nq < 0 || a->Nk < 0 || a->D < 1)
+    return FA_ERR_SHAPE;
+  if (a->Hq > kMaxHeads || a->Hkv > a->Hq || a->Hq % a->Hkv != 0) return FA_ERR_SHAPE;
+  if (a->block != 64 || a->D != 128) return FA_ERR_UNSUPPORTED;
+  if (a->out_dtype != FA_BF16 && a->out_dtype != FA_F32) return FA_ERR_DTYPE;
+  if (!scale_ok(a->scale)) return FA_ERR_ARG;
+  if (a->causal != 0 && a->causal != 1) return FA_ERR_ARG;
+  if (a->Nq == 0) return FA_OK;
+  if (!a->q || !a->o || !a->q_scales) return FA_ERR_NULL_PTR;
+  if (a->Nk > 0 && (!a->k || !a->v || !a->k_scales)) return FA_ERR_NULL_PTR;
+  const int ob = a->out_dtype == FA_BF16 ? 2 : 4;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return FA_ERR_STRIDE;
+  if (!strides_ok(a->q_stride, 3, 1) || !strides_ok(a->k_stride, 3, 1) ||
+      !strides_ok(a->v_stride, 3, 2) || !strides_ok(a->o_stride, 3, ob))
+    return FA_ERR_STRIDE;
+  if ((reinterpret_cast<uintptr_t>(a->q_scales) & 3u) || (reinterpret_cast<uintptr_t>(a->k_scales) & 3u))
+    return FA_ERR_STRIDE;
+  if (a->lse && (reinterpret_cast<uintptr_t>(a->lse) & 3u)) return FA_ERR_STRIDE;
+  return FA_OK;
+}
+
 int paged_nsplit(const fa_decode_paged_args* a) {
   return a->max_len <= 0 ? 0 : (a->max_len + a->split_len - 1) / a->split_len;
 }
@@ -320,6 +357,48 @@ fa_status fa_decode(const fa_decode_args* a, void* workspace, size_t ws_bytes, v
   p.scale_log2 = a->scale * 1.4426950408889634f;
   return map_launch_error(
       fa::launch_decode(p, a->D, a->out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_quantize_fp8(const fa_quantize_fp8_args* a, void* stream) {
+  const fa_status st = validate_quantize(a);
+  if (st != FA_OK || a->N == 0) return st;
+  fa::QuantParams p{};
+  p.x = static_cast<const uint16_t*>(a->x);
+  p.codes = static_cast<uint8_t*>(a->codes);
+  p.scales = a->scales;
+  p.xs0 = a->x_stride[0], p.xs1 = a->x_stride[1], p.xs2 = a->x_stride[2];
+  p.cs0 = a->codes_stride[0], p.cs1 = a->codes_stride[1], p.cs2 = a->codes_stride[2];
+  p.B = a->B, p.H = a->H, p.N = a->N;
+  p.nb = (a->N + a->block - 1) / a->block;
+  return map_launch_error(fa::launch_quantize_fp8(p, a->D, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd_fp8(const fa_fwd_fp8_args* a, void* stream) {
+  const fa_status st = validate_fwd_fp8(a);
+  if (st != FA_OK || a->Nq == 0) return st;
+  fa::FwdParams p{};
+  p.q = static_cast<const uint16_t*>(a->q);  // E4M3 codes; strides below are in bytes
+  p.k = static_cast<const uint16_t*>(a->k);
+  p.v = static_cast<const uint16_t*>(a->v);
+  p.o = a->o;
+  p.lse = a->lse;
+  p.kv_lens = a->kv_lens;
+  p.q_scale = a->q_scales;
+  p.k_scale = a->k_scales;
+  const int nqb = (a->Nq + 63) / 64, nkb = (a->Nk + 63) / 64;
+  p.qsc_b = (int64_t)a->Hq * nqb, p.qsc_h = nqb;
+  p.ksc_b = (int64_t)a->Hkv * nkb, p.ksc_h = nkb;
+  p.qs0 = a->q_stride[0], p.qs1 = a->q_stride[1], p.qs2 = a->q_stride[2];
+  p.ks0 = a->k_stride[0], p.ks1 = a->k_stride[1], p.ks2 = a->k_stride[2];
+  p.vs0 = a->v_stride[0], p.vs1 = a->v_stride[1], p.vs2 = a->v_stride[2];
+  p.os0 = a->o_stride[0], p.os1 = a->o_stride[1], p.os2 = a->o_stride[2];
+  p.lse_sb = (int64_t)a->Hq * a->Nq, p.lse_sh = a->Nq;
+  p.B = a->B, p.Hq = a->Hq, p.Hkv = a->Hkv, p.Nq = a->Nq, p.Nk = a->Nk;
+  p.G = a->Hq / a->Hkv;
+  p.scale = a->scale;
+  p.scale_log2 = a->scale * 1.4426950408889634f;
+  p.causal = a->causal;
+  return map_launch_error(fa::launch_fwd_fp8(p, a->out_dtype, static_cast<hipStream_t>(stream)));
 }
 
 size_t fa_decode_paged_workspace_bytes(const fa_decode_paged_args* a) {

@@ -16,6 +16,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -28,6 +29,17 @@ constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, each with its
 __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+// 32x32x64 MFMA on OCP E4M3 operands (format code 0 for both), unscaled, fp32
+// accumulate.  Lane l holds row (A) / column (B) l % 32 and 32 bytes of the k range;
+// byte b of lane half h in A multiplies byte b of the same half in B, so any
+// assignment of k to (half, byte) works as long as both operands use the same one.
+// The result registers are laid out as those of the bf16 32x32x16 product.
+__device__ __forceinline__ f32x16_t mfma32_f8(i32x8_t a, i32x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ i32x8_t cat8(u32x4_t a, u32x4_t b) {
+  return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Two floats -> packed bf16 pair (round to nearest even); `lo` in the low half.
@@ -103,11 +115,13 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, u
 // FA_WAIT_VMCNT for a compile-time count (the counts the ring pipelines use).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N == 0 || N == 1 || N == 2 || N == 4 || N == 5 || N == 8 || N == 9 || N == 16,
+  static_assert(N == 0 || N == 1 || N == 2 || N == 3 || N == 4 || N == 5 || N == 8 || N == 9 ||
+                    N == 16,
                 "add the count here");
   if constexpr (N == 0) FA_WAIT_VMCNT(0);
   else if constexpr (N == 1) FA_WAIT_VMCNT(1);
   else if constexpr (N == 2) FA_WAIT_VMCNT(2);
+  else if constexpr (N == 3) FA_WAIT_VMCNT(3);
   else if constexpr (N == 4) FA_WAIT_VMCNT(4);
   else if constexpr (N == 5) FA_WAIT_VMCNT(5);
   else if constexpr (N == 8) FA_WAIT_VMCNT(8);

@@ -38,7 +38,12 @@
 //  * workgroups are ordered so tiles that share a KV head run on the same XCD;
 //  * a packed batch of variable-length sequences (self-test page, section C) runs the
 //    same kernel: each workgroup takes its sequence's row range from the offsets, and
-//    tiles past a short sequence exit at once.
+//    tiles past a short sequence exit at once;
+//  * FP8 Q K^T (V2/V3 article, section FP8低精度): Q and K arrive as E4M3 codes with one
+//    step per 64-row block; S^T = K Q^T runs on the 32x32x64 E4M3 MFMA with fp32
+//    accumulation (half the bf16 product's time), K blocks are staged at one byte per
+//    element, and the two blocks' steps fold into the exp2 coefficient of each block, so
+//    the softmax, P V and the epilogue are those of the bf16 path.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -51,19 +56,28 @@ constexpr int kFwdBR = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBC = 64;              // keys per block
 constexpr int kFwdSlots = 4;            // ring depth for K and for V
 
-template <int D>
+// QK8: K (and Q) are E4M3 codes, one byte per element; V stays bf16.
+template <int D, bool QK8 = false>
 struct FwdTile {
-  static constexpr int KS = D / 16;              // k-steps of S^T = K Q^T
+  static constexpr int KS = D / 16;              // k-steps of S^T = K Q^T (bf16)
+  static constexpr int KS8 = D / 64;             // k-steps of S^T = K Q^T (E4M3)
   static constexpr int DB = D / 32;              // 32-row blocks of O^T
-  static constexpr int ROWB = D * 2;             // bytes per K/V row
-  static constexpr int SPR = D / 8;              // 16-byte slots per row
-  static constexpr int RPB = 256 / ROWB;         // rows per 256-byte LDS bank period
-  static constexpr int RPI = 1024 / ROWB;        // rows per wave DMA instruction
-  static constexpr int TBYTES = kFwdBC * ROWB;   // one K or V block in LDS
-  static constexpr int NDMA = TBYTES / (1024 * kFwdWaves);  // DMA instructions per thread
-  static constexpr int LDS_BYTES = 2 * kFwdSlots * TBYTES;
+  static constexpr int ROWB = D * 2;             // bytes per V row
+  static constexpr int SPR = D / 8;              // 16-byte slots per V row
+  static constexpr int RPB = 256 / ROWB;         // V rows per 256-byte LDS bank period
+  static constexpr int RPI = 1024 / ROWB;        // V rows per wave DMA instruction
+  static constexpr int KROWB = QK8 ? D : 2 * D;  // bytes per staged K row
+  static constexpr int KSPR = KROWB / 16;
+  static constexpr int KRPB = 256 / KROWB;
+  static constexpr int KRPI = 1024 / KROWB;
+  static constexpr int TBYTES = kFwdBC * ROWB;   // one V block in LDS
+  static constexpr int KTBYTES = kFwdBC * KROWB; // one K block in LDS
+  static constexpr int NDMA = TBYTES / (1024 * kFwdWaves);    // V DMA instructions per thread
+  static constexpr int NDMA_K = KTBYTES / (1024 * kFwdWaves); // K DMA instructions per thread
+  static constexpr int LDS_BYTES = kFwdSlots * (KTBYTES + TBYTES);
   static_assert(NDMA * 1024 * kFwdWaves == TBYTES, "a block must split evenly over the waves");
-  static __device__ __forceinline__ int swz_k(int r) { return (r / RPB) % SPR; }
+  static_assert(NDMA_K * 1024 * kFwdWaves == KTBYTES, "a block must split evenly over the waves");
+  static __device__ __forceinline__ int swz_k(int r) { return (r / KRPB) % KSPR; }
   static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPB) % (SPR / 4)); }
 };
 
@@ -81,14 +95,15 @@ struct Slot {
 // LSE = m*scale + ln(l) use the same reference, so the result does not depend on it.
 constexpr float kMaxBlockSum = 256.f;
 
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool QK8>
 __global__ void __launch_bounds__(64 * kFwdWaves) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_bf16_kernel(FwdParams p) {
-  using T = FwdTile<D>;
+  using T = FwdTile<D, QK8>;
+  static_assert(!QK8 || D == 128, "the E4M3 path is built for D = 128");
   constexpr int BR = kFwdBR, BC = kFwdBC, NW = kFwdWaves, NS = kFwdSlots;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[T::LDS_BYTES];
   unsigned char* kring = lds;
-  unsigned char* vring = lds + NS * T::TBYTES;
+  unsigned char* vring = lds + NS * T::KTBYTES;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -148,36 +163,54 @@ fwd_bf16_kernel(FwdParams p) {
     return;  // uniform over the workgroup
   }
 
-  // ---- Q^T fragments (B operand), loaded once; rows past Nq read as zero
-  u32x4_t qf[T::KS];
+  // ---- Q^T fragments (B operand), loaded once; rows past Nq read as zero.  bf16: the
+  // lane's 8-element slot 2 s + hi of its query row for k-step s; E4M3: the lane's 32
+  // bytes 64 s + 32 hi .. of its row for k-step s (the K operand uses the same bytes)
+  u32x4_t qf[QK8 ? 1 : T::KS];
+  i32x8_t qf8[QK8 ? T::KS8 : 1];
+  float dqw = 1.f;  // E4M3: the step of this wave's 64-row query block
   {
-    const int64_t qpitch = p.qs2 * 2;
-    const uint16_t* qtile = p.q + b * p.qs0 + hq * p.qs1 + (qr0 + q_wg0) * p.qs2;
-    const auto rq = make_rsrc(qtile, rows_span(min(BR, nq - q_wg0), qpitch, D * 2));
-    const uint32_t off = (uint32_t)((wave * 32 + l32) * qpitch) + 16 * hi;
+    const int64_t qpitch = p.qs2 * (QK8 ? 1 : 2);
+    const unsigned char* qtile = reinterpret_cast<const unsigned char*>(p.q) +
+                                 (b * p.qs0 + hq * p.qs1 + (qr0 + q_wg0) * p.qs2) * (QK8 ? 1 : 2);
+    const auto rq = make_rsrc(qtile, rows_span(min(BR, nq - q_wg0), qpitch, T::KROWB));
+    if constexpr (QK8) {
+      const uint32_t off = (uint32_t)((wave * 32 + l32) * qpitch) + 32 * hi;
 #pragma unroll
-    for (int s = 0; s < T::KS; ++s) qf[s] = buf_load16(rq, off + 32 * s);
+      for (int s = 0; s < T::KS8; ++s)
+        qf8[s] = cat8(buf_load16(rq, off + 64 * s), buf_load16(rq, off + 64 * s + 16));
+      // (a wave whose rows all lie past Nq takes the last block's step; its rows are
+      // never stored)
+      const int qblk = min((q_wg0 + 32 * wave) / 64, (nq + 63) / 64 - 1);
+      dqw = p.q_scale[b * p.qsc_b + hq * p.qsc_h + qblk];
+    } else {
+      const uint32_t off = (uint32_t)((wave * 32 + l32) * qpitch) + 16 * hi;
+#pragma unroll
+      for (int s = 0; s < T::KS; ++s) qf[s] = buf_load16(rq, off + 32 * s);
+    }
     asm volatile("" ::: "memory");  // issue these before the ring loads below
   }
 
-  const uint16_t* kbase = p.k + b * p.ks0 + hkv * p.ks1 + kr0 * p.ks2;
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) +
+                               (b * p.ks0 + hkv * p.ks1 + kr0 * p.ks2) * (QK8 ? 1 : 2);
   const uint16_t* vbase = p.v + b * p.vs0 + hkv * p.vs1 + kr0 * p.vs2;
-  const int64_t kpitch = p.ks2 * 2, vpitch = p.vs2 * 2;
+  const int64_t kpitch = p.ks2 * (QK8 ? 1 : 2), vpitch = p.vs2 * 2;
 
   // DMA: thread (wave w, lane) fills, for instruction i, row RPI (NW i + w) + lane / SPR,
   // slot lane % SPR, with the swizzled 16-byte chunk of that row; the swizzle of that
   // row does not depend on i, and the row step of i goes into the scalar offset.
   const int drow = T::RPI * wave + lane / T::SPR, dslot = lane % T::SPR;
-  const uint32_t kdma = (uint32_t)(drow * kpitch) + 16 * (dslot ^ T::swz_k(drow));
+  const int krow_d = T::KRPI * wave + lane / T::KSPR, kslot_d = lane % T::KSPR;
+  const uint32_t kdma = (uint32_t)(krow_d * kpitch) + 16 * (kslot_d ^ T::swz_k(krow_d));
   const uint32_t vdma = (uint32_t)(drow * vpitch) + 16 * (dslot ^ T::swz_v(drow));
-  const int kstep = (int)(NW * T::RPI * kpitch), vstep = (int)(NW * T::RPI * vpitch);
+  const int kstep = (int)(NW * T::KRPI * kpitch), vstep = (int)(NW * T::RPI * vpitch);
 
   auto dma_k = [&](int blk, int slot) {  // blocks past the keys fill the slot with zeros
     const int key0 = blk * BC;
-    const auto rk = make_rsrc(kbase + (int64_t)key0 * p.ks2, rows_span(min(BC, lk - key0), kpitch, D * 2));
-    unsigned char* dst = kring + slot * T::TBYTES + 1024 * wave;
+    const auto rk = make_rsrc(kbase + (int64_t)key0 * kpitch, rows_span(min(BC, lk - key0), kpitch, T::KROWB));
+    unsigned char* dst = kring + slot * T::KTBYTES + 1024 * wave;
 #pragma unroll
-    for (int i = 0; i < T::NDMA; ++i) lds_dma16(rk, dst + 1024 * NW * i, kdma, 0, kstep * i);
+    for (int i = 0; i < T::NDMA_K; ++i) lds_dma16(rk, dst + 1024 * NW * i, kdma, 0, kstep * i);
   };
   auto dma_v = [&](int blk, int slot) {
     const int key0 = blk * BC;
@@ -187,19 +220,33 @@ fwd_bf16_kernel(FwdParams p) {
     for (int i = 0; i < T::NDMA; ++i) lds_dma16(rv, dst + 1024 * NW * i, vdma, 0, vstep * i);
   };
 
-  // S^T operand reads: rows l32 and 32 + l32 (same swizzle), logical slot 2 ks + hi
-  const int krow = l32 * T::ROWB, ksw = T::swz_k(l32);
+  // S^T operand reads: rows l32 and 32 + l32 (same swizzle); bf16: logical slot
+  // 2 ks + hi; E4M3: logical slots 4 s + 2 hi and 4 s + 2 hi + 1 (32 bytes)
+  const int krow = l32 * T::KROWB, ksw = T::swz_k(l32);
   auto qk = [&](int slot, f32x16_t& s0, f32x16_t& s1) {
-    const unsigned char* ks = kring + slot * T::TBYTES + krow;
+    const unsigned char* ks = kring + slot * T::KTBYTES + krow;
     s0 = f32x16_t{};
     s1 = f32x16_t{};
+    if constexpr (QK8) {
 #pragma unroll
-    for (int k = 0; k < T::KS; ++k) {
-      const int o = 16 * ((2 * k + hi) ^ ksw);
-      const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(ks + o);
-      const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(ks + 32 * T::ROWB + o);
-      s0 = mfma32(a0, qf[k], s0);
-      s1 = mfma32(a1, qf[k], s1);
+      for (int k = 0; k < T::KS8; ++k) {
+        const int o0 = 16 * ((4 * k + 2 * hi) ^ ksw), o1 = 16 * ((4 * k + 2 * hi + 1) ^ ksw);
+        const i32x8_t a0 = cat8(*reinterpret_cast<const u32x4_t*>(ks + o0),
+                                *reinterpret_cast<const u32x4_t*>(ks + o1));
+        const i32x8_t a1 = cat8(*reinterpret_cast<const u32x4_t*>(ks + 32 * T::KROWB + o0),
+                                *reinterpret_cast<const u32x4_t*>(ks + 32 * T::KROWB + o1));
+        s0 = mfma32_f8(a0, qf8[k], s0);
+        s1 = mfma32_f8(a1, qf8[k], s1);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < T::KS; ++k) {
+        const int o = 16 * ((2 * k + hi) ^ ksw);
+        const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(ks + o);
+        const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(ks + 32 * T::KROWB + o);
+        s0 = mfma32(a0, qf[k], s0);
+        s1 = mfma32(a1, qf[k], s1);
+      }
     }
   };
 
@@ -216,8 +263,13 @@ fwd_bf16_kernel(FwdParams p) {
   f32x16_t acc[T::DB];
 #pragma unroll
   for (int d = 0; d < T::DB; ++d) acc[d] = f32x16_t{};
-  float m = -INFINITY, l = 0.f;  // m: exponent reference (raw score units)
+  float m = -INFINITY, l = 0.f;  // m: exponent reference (unscaled q.k units)
   const float c = p.scale_log2;
+  // E4M3: the MFMA gives q_hat.k_hat; a block's scores are that times dqw * (its key
+  // block's step).  The steps are read one block ahead with scalar loads.
+  const auto* kscl = (const __attribute__((address_space(4))) float*)(
+      QK8 ? p.k_scale + b * p.ksc_b + hkv * p.ksc_h : p.k_scale);
+  float dk_next = QK8 ? kscl[0] : 1.f;
 
   // One block: (s0, s1) hold the scores of block j (keys 64 j + [0, 32), + [32, 64));
   // the scores of block j + 1 are produced into (n0, n1).
@@ -228,6 +280,12 @@ fwd_bf16_kernel(FwdParams p) {
     // K_{j+3} and V_{j+2} into the slots of K_{j-1} and V_{j-2}, which are free
     dma_k(j + 3, (sl + 3) % NS);
     dma_v(j + 2, (sl + 2) % NS);
+    float sq = 1.f;  // score units per MFMA unit of this block
+    if constexpr (QK8) {
+      sq = dqw * dk_next;
+      dk_next = kscl[min(j + 1, nblk - 1)];
+    }
+    const float cb = c * sq;
 
     const int key0 = j * BC;
     const bool edge = (key0 + BC > lk) || (p.causal && key0 + BC - 1 > q_wg0 + diag);
@@ -256,8 +314,8 @@ fwd_bf16_kernel(FwdParams p) {
       float rs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(fmaf(a0[r], c, -mc)), p1 = fast_exp2(fmaf(a0[r + 1], c, -mc));
-        const float p2 = fast_exp2(fmaf(a1[r], c, -mc)), p3 = fast_exp2(fmaf(a1[r + 1], c, -mc));
+        const float p0 = fast_exp2(fmaf(a0[r], cb, -mc)), p1 = fast_exp2(fmaf(a0[r + 1], cb, -mc));
+        const float p2 = fast_exp2(fmaf(a1[r], cb, -mc)), p3 = fast_exp2(fmaf(a1[r + 1], cb, -mc));
         rs += (p0 + p1) + (p2 + p3);
         pf[r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
         pf[2 + (r >> 3)][(r & 7) >> 1] = pack_bf16(p2, p3);
@@ -277,7 +335,7 @@ fwd_bf16_kernel(FwdParams p) {
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
-      mx = halves_max(mx);
+      mx = halves_max(mx) * sq;
       const float m_new = fmaxf(m, mx);
       const float alpha = m == -INFINITY ? 0.f : fast_exp2((m - m_new) * c);
       l *= alpha;
@@ -307,7 +365,7 @@ fwd_bf16_kernel(FwdParams p) {
     // the loads of blocks j + 2 (K) and j + 1 (V), issued one block ago, have landed
     // (only this block's may still be in flight); the barrier then publishes them and
     // frees the slots this block read
-    if constexpr (T::NDMA == 2) FA_WAIT_VMCNT(4); else FA_WAIT_VMCNT(2);
+    wait_vmcnt<T::NDMA + T::NDMA_K>();
     FA_WAIT_LGKMCNT0();
     FA_BARRIER();
   };
@@ -493,10 +551,20 @@ hipError_t launch_fwd(const FwdParams& p0, int in_dtype, int out_dtype, int D, h
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const bool of32 = out_dtype == FA_F32;
   if (D == 128)
-    return of32 ? launch(fwd_bf16_kernel<128, true>, (int)grid, 64 * kFwdWaves, p, stream)
-                : launch(fwd_bf16_kernel<128, false>, (int)grid, 64 * kFwdWaves, p, stream);
-  return of32 ? launch(fwd_bf16_kernel<64, true>, (int)grid, 64 * kFwdWaves, p, stream)
-              : launch(fwd_bf16_kernel<64, false>, (int)grid, 64 * kFwdWaves, p, stream);
+    return of32 ? launch(fwd_bf16_kernel<128, true, false>, (int)grid, 64 * kFwdWaves, p, stream)
+                : launch(fwd_bf16_kernel<128, false, false>, (int)grid, 64 * kFwdWaves, p, stream);
+  return of32 ? launch(fwd_bf16_kernel<64, true, false>, (int)grid, 64 * kFwdWaves, p, stream)
+              : launch(fwd_bf16_kernel<64, false, false>, (int)grid, 64 * kFwdWaves, p, stream);
+}
+
+hipError_t launch_fwd_fp8(const FwdParams& p0, int out_dtype, hipStream_t stream) {
+  FwdParams p = p0;
+  p.nqt = (p.Nq + kFwdBR - 1) / kFwdBR;
+  const int64_t grid = (int64_t)p.nqt * p.Hq * p.B;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  return out_dtype == FA_F32
+             ? launch(fwd_bf16_kernel<128, true, true>, (int)grid, 64 * kFwdWaves, p, stream)
+             : launch(fwd_bf16_kernel<128, false, true>, (int)grid, 64 * kFwdWaves, p, stream);
 }
 
 }  // namespace fa

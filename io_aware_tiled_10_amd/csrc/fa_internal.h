@@ -21,12 +21,29 @@ struct FwdParams {
   int total_q, total_k;
   int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
   int64_t lse_sb, lse_sh;  // LSE element of (b, h, row): b * lse_sb + h * lse_sh + row
+  // FP8 Q K^T: q and k hold E4M3 codes (strides in bytes); the step of each 64-row block
+  // is q_scale[b * qsc_b + h * qsc_h + row / 64] (k_scale likewise, per KV head)
+  const float* q_scale;
+  const float* k_scale;
+  int64_t qsc_b, qsc_h, ksc_b, ksc_h;
   int B, Hq, Hkv, Nq, Nk, G, nqt;  // packed batches: Nq = longest sequence
   float scale, scale_log2;
   int causal;
 };
 
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int out_dtype, int D, hipStream_t stream);
+// Q and K as E4M3 codes with per-64-row steps, V bf16 (D = 128).
+hipError_t launch_fwd_fp8(const FwdParams& p, int out_dtype, hipStream_t stream);
+
+// E4M3 block quantisation of a bf16 [B, H, N, D] tensor.
+struct QuantParams {
+  const uint16_t* x;
+  uint8_t* codes;
+  float* scales;  // contiguous [B, H, nb]
+  int64_t xs0, xs1, xs2, cs0, cs1, cs2;
+  int B, H, N, nb;
+};
+hipError_t launch_quantize_fp8(const QuantParams& p, int D, hipStream_t stream);
 
 // Backward.
 struct BwdParams {

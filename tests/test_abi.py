@@ -27,7 +27,7 @@ FAKE = 0x7F0000000000  # a 16-byte aligned address that is never dereferenced
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_header_declares_the_expected_calls():
@@ -232,3 +232,44 @@ def test_decode_paged_workspace_query():
     assert need == rows * 128 * 4 + rows * 4
     assert fb.lib().fa_decode_paged(ctypes.byref(a), FAKE, need - 1, None) == WS
     assert fb.lib().fa_decode_paged(ctypes.byref(good_paged(Bs=0)), None, 0, None) == OK
+
+
+def good_quant(**kw):
+    a = fb.QuantizeArgs(x=FAKE, codes=FAKE, scales=FAKE, x_stride=fb.c_i64x3(4 * 100 * 128, 100 * 128, 128),
+                        codes_stride=fb.c_i64x3(4 * 100 * 128, 100 * 128, 128), B=1, H=4, N=100, D=128, block=64)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+QUANT_BAD = [({"B": 0}, SHAPE), ({"N": -1}, SHAPE), ({"block": 32}, UNSUP), ({"D": 64}, UNSUP),
+             ({"x": None}, NULL), ({"scales": None}, NULL), ({"codes": FAKE + 8}, STRIDE),
+             ({"codes_stride": fb.c_i64x3(0, 0, 120)}, STRIDE), ({"scales": FAKE + 2}, STRIDE)]
+
+
+@pytest.mark.parametrize("change,status", QUANT_BAD)
+def test_quantize_fp8_rejects_bad_arguments(change, status):
+    assert fb.lib().fa_quantize_fp8(ctypes.byref(good_quant(**change)), None) == status
+
+
+def good_fp8(**kw):
+    st8 = fb.c_i64x3(2 * 8 * 128, 8 * 128, 128)
+    st = fb.c_i64x3(2 * 8 * 128, 8 * 128, 128)
+    a = fb.FwdFp8Args(q=FAKE, k=FAKE, v=FAKE, q_scales=FAKE, k_scales=FAKE, o=FAKE, lse=FAKE, kv_lens=None,
+                      q_stride=st8, k_stride=st8, v_stride=st, o_stride=st, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, D=128,
+                      block=64, out_dtype=fb.FA_BF16, scale=0.088, causal=0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+FP8_BAD = [({"D": 64}, UNSUP), ({"block": 128}, UNSUP), ({"Hq": 3, "Hkv": 2}, SHAPE), ({"out_dtype": 6}, DTYPE),
+           ({"scale": 0.0}, ARG), ({"causal": 5}, ARG), ({"q_scales": None}, NULL), ({"k_scales": None}, NULL),
+           ({"v": None}, NULL), ({"q": FAKE + 4}, STRIDE), ({"q_stride": fb.c_i64x3(0, 0, 100)}, STRIDE),
+           ({"k_scales": FAKE + 1}, STRIDE)]
+
+
+@pytest.mark.parametrize("change,status", FP8_BAD)
+def test_fwd_fp8_rejects_bad_arguments(change, status):
+    assert fb.lib().fa_fwd_fp8(ctypes.byref(good_fp8(**change)), None) == status
+    assert fb.lib().fa_fwd_fp8(ctypes.byref(good_fp8(Nq=0)), None) == OK
