@@ -15,7 +15,8 @@ inputs already resident in HBM:
           lengths U[1024, 32768] (seed 0), chunks of 2048 + merge
 
 --aux also times, outside the step: the B4 H16 N2048 D128 forwards (non-causal and
-causal), the long forward with E4M3 Q and K (and the quantisation passes), the GQA backward at B1 Hq32 Hkv8 N16384 D128 causal, a packed variable-length causal forward (32 sequences of U[256, 4096] rows,
+causal), the forward and backward workloads with dropout p = 0.1, the long forward with E4M3
+Q and K (and the quantisation passes), the GQA backward at B1 Hq32 Hkv8 N16384 D128 causal, a packed variable-length causal forward (32 sequences of U[256, 4096] rows,
 Hq32 Hkv8 D128) and the decode workload read from page pools of 16 and of 256 rows
 in random page order through a block table.
 
@@ -184,6 +185,24 @@ class FwdFp8Leg:
     def quantize(self):
         fa.quantize_fp8(self.q, out=self.q8, scales_out=self.qs)
         fa.quantize_fp8(self.k, out=self.k8, scales_out=self.ks)
+
+
+class DropoutLegs:
+    """The forward and backward workloads with dropout p = 0.1 on P (Philox mask)."""
+    P_DROP, SEED = 0.1, 0x5EED
+
+    def __init__(self, fwd: FwdLeg, bwd: BwdLeg):
+        self.f, self.b = fwd, bwd
+        self.o, self.lse = fa.fwd_dropout(bwd.q, bwd.k, bwd.v, self.P_DROP, self.SEED, causal=bwd.cfg["causal"])
+
+    def run_fwd(self):
+        f = self.f
+        fa.fwd_dropout(f.q, f.k, f.v, self.P_DROP, self.SEED, causal=f.cfg["causal"], out=f.o, lse_out=f.lse)
+
+    def run_bwd(self):
+        b = self.b
+        fa.bwd_dropout(b.q, b.k, b.v, self.o, b.do, self.lse, self.P_DROP, self.SEED, causal=b.cfg["causal"],
+                       workspace=b.ws, grads=b.grads)
 
 
 class DecodePagedLeg:
@@ -470,6 +489,19 @@ def main():
             leg = FwdLeg(cfg)
             out_legs[name] = flops_rec(leg, time_aux(leg, stream))
             del leg
+        fl = legs["fwd"] if "fwd" in legs else FwdLeg(FWD_CFG)
+        bl = legs["bwd"] if "bwd" in legs else BwdLeg(BWD_CFG)
+        dl = DropoutLegs(fl, bl)
+
+        class _F:
+            run = dl.run_fwd
+
+        class _B:
+            run = dl.run_bwd
+        _F.flops, _B.flops = fl.flops, bl.flops
+        out_legs["fwd_dropout_p0.1"] = flops_rec(_F, time_aux(_F, stream))
+        out_legs["bwd_dropout_p0.1"] = flops_rec(_B, time_aux(_B, stream))
+        del dl
         leg = FwdFp8Leg(FWD_CFG)
         rec = flops_rec(leg, time_aux(leg, stream))
 

@@ -25,6 +25,9 @@
  *                    (prefix offsets instead of padding).
  *                    Pages: self-test page, section C (padding masks and variable-length
  *                    sequences).
+ *   fa_fwd_dropout / fa_bwd_dropout  the forward and backward with dropout on P, the
+ *                    mask regenerated from a counter-based generator (Philox4x32-10).
+ *                    Pages: self-test page, section C.
  *   fa_quantize_fp8  two-pass E4M3 block quantisation of Q or K (step = block max / 448).
  *   fa_fwd_fp8       the forward with Q K^T on the E4M3 matrix cores (fp32 accumulation).
  *                    Pages: V2/V3 article, section FP8低精度 and its formula block.
@@ -205,6 +208,25 @@ typedef struct fa_decode_args {
 size_t fa_decode_workspace_bytes(const fa_decode_args *args);
 fa_status fa_decode(const fa_decode_args *args, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Forward and backward with dropout on P (bf16, D in {64, 128}).
+ * Pages: self-test page, section C (how dropout is done without storing the mask).
+ *   args, workspace: as fa_fwd / fa_bwd
+ *   p_drop  dropout probability in [0, 1), taken in steps of 1/256: t = round(256 p);
+ *           t == 0 runs the plain call
+ *   seed    64-bit key of the mask generator
+ * Element (b, h, i, j) is kept iff byte 4a + e of Philox4x32-10(counter = (2 (j / 32) +
+ * (j / 4) % 2, i, h, b), key = (seed low, seed high)) is >= t, with a = (j / 8) % 4,
+ * e = j % 4 and byte n at bits 8 (n % 4) of word n / 4; kept probabilities are scaled
+ * by 256 / (256 - t).  O = (P * mask * scale) V; LSE is that of the undropped scores.
+ * The backward regenerates the same mask (pass the forward's p_drop and seed):
+ * dV = (P * mask * scale)^T dO, dP = (dO V^T) * mask * scale, D_i = rowsum(dO * O).
+ * FA_ERR_ARG for p_drop outside [0, 1); FA_ERR_UNSUPPORTED for fp32 inputs.
+ * ------------------------------------------------------------------------------- */
+fa_status fa_fwd_dropout(const fa_fwd_args *args, float p_drop, uint64_t seed, void *stream);
+fa_status fa_bwd_dropout(const fa_bwd_args *args, float p_drop, uint64_t seed, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Forward over a packed batch of B variable-length sequences (bf16, D in {64, 128}).

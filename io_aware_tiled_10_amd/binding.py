@@ -112,7 +112,8 @@ class FwdFp8Args(ctypes.Structure):
     ]
 
 
-EXPORTED = ["fa_fwd", "fa_fwd_varlen", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd", "fa_bwd_workspace_bytes",
+EXPORTED = ["fa_fwd", "fa_fwd_dropout", "fa_fwd_varlen", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd",
+            "fa_bwd_dropout", "fa_bwd_workspace_bytes",
             "fa_decode", "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
             "fa_status_str", "fa_device_supported", "fa_version"]
 
@@ -145,6 +146,11 @@ def lib() -> ctypes.CDLL:
         h.fa_decode_paged.restype = ctypes.c_int
         h.fa_decode_paged_workspace_bytes.argtypes = [ctypes.POINTER(DecodePagedArgs)]
         h.fa_decode_paged_workspace_bytes.restype = ctypes.c_size_t
+        h.fa_fwd_dropout.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_float, ctypes.c_uint64, ctypes.c_void_p]
+        h.fa_fwd_dropout.restype = ctypes.c_int
+        h.fa_bwd_dropout.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_float, ctypes.c_uint64, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p]
+        h.fa_bwd_dropout.restype = ctypes.c_int
         h.fa_quantize_fp8.argtypes = [ctypes.POINTER(QuantizeArgs), ctypes.c_void_p]
         h.fa_quantize_fp8.restype = ctypes.c_int
         h.fa_fwd_fp8.argtypes = [ctypes.POINTER(FwdFp8Args), ctypes.c_void_p]
@@ -322,6 +328,36 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib().fa_bwd(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return dq, dk, dv
+
+
+def fwd_dropout(q, k, v, p_drop: float, seed: int, causal: bool = False, scale: Optional[float] = None,
+                kv_lens: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                with_lse: bool = True, out: Optional[torch.Tensor] = None,
+                lse_out: Optional[torch.Tensor] = None):
+    """Forward with dropout on P via ``fa_fwd_dropout`` (mask from Philox4x32-10 and ``seed``)."""
+    B, Hq, Nq, D = q.shape
+    o = out if out is not None else torch.empty((B, Hq, Nq, D), dtype=out_dtype or q.dtype, device=q.device)
+    lse = lse_out if lse_out is not None else (
+        torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if with_lse else None)
+    a = fwd_args(q, k, v, o, lse, causal, scale, kv_lens)
+    _check(lib().fa_fwd_dropout(ctypes.byref(a), float(p_drop), int(seed), _stream(q.device)))
+    return o, lse
+
+
+def bwd_dropout(q, k, v, o, do, lse, p_drop: float, seed: int, causal: bool = False,
+                scale: Optional[float] = None, kv_lens: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None,
+                grads: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Backward of ``fwd_dropout`` (same p_drop and seed) via ``fa_bwd_dropout``."""
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k),
+                                                  torch.empty_like(v))
+    a = bwd_args(q, k, v, o, do, lse, dq, dk, dv, causal, scale, kv_lens)
+    need = lib().fa_bwd_workspace_bytes(ctypes.byref(a))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().fa_bwd_dropout(ctypes.byref(a), float(p_drop), int(seed), _ptr(workspace), workspace.numel(),
+                                _stream(q.device)))
     return dq, dk, dv
 
 

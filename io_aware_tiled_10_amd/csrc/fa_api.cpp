@@ -259,6 +259,44 @@ fa_status fa_fwd(const fa_fwd_args* a, void* stream) {
       fa::launch_fwd(p, a->in_dtype, a->out_dtype, a->D, static_cast<hipStream_t>(stream)));
 }
 
+// Dropout threshold t = round(256 p) in [0, 255], or -1 when p is not in [0, 1).
+int dropout_threshold(float p_drop) {
+  if (!(p_drop >= 0.f && p_drop < 1.f)) return -1;
+  const int t = (int)std::floor(p_drop * 256.0 + 0.5);
+  return t < 0 ? 0 : (t > 255 ? 255 : t);
+}
+
+fa_status fa_fwd_dropout(const fa_fwd_args* a, float p_drop, uint64_t seed, void* stream) {
+  fa_status st = validate_fwd(a);
+  if (st != FA_OK) return st;
+  if (a->in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  const int t = dropout_threshold(p_drop);
+  if (t < 0) return FA_ERR_ARG;
+  if (t == 0) return fa_fwd(a, stream);  // nothing is dropped
+  if (a->Nq == 0) return FA_OK;
+  fa::FwdParams p{};
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.k = static_cast<const uint16_t*>(a->k);
+  p.v = static_cast<const uint16_t*>(a->v);
+  p.o = a->o;
+  p.lse = a->lse;
+  p.kv_lens = a->kv_lens;
+  p.qs0 = a->q_stride[0], p.qs1 = a->q_stride[1], p.qs2 = a->q_stride[2];
+  p.ks0 = a->k_stride[0], p.ks1 = a->k_stride[1], p.ks2 = a->k_stride[2];
+  p.vs0 = a->v_stride[0], p.vs1 = a->v_stride[1], p.vs2 = a->v_stride[2];
+  p.os0 = a->o_stride[0], p.os1 = a->o_stride[1], p.os2 = a->o_stride[2];
+  p.lse_sb = (int64_t)a->Hq * a->Nq, p.lse_sh = a->Nq;
+  p.B = a->B, p.Hq = a->Hq, p.Hkv = a->Hkv, p.Nq = a->Nq, p.Nk = a->Nk;
+  p.G = a->Hq / a->Hkv;
+  p.scale = a->scale;
+  p.scale_log2 = a->scale * 1.4426950408889634f;
+  p.causal = a->causal;
+  p.drop_t = (uint32_t)t;
+  p.drop_scale = 256.f / (float)(256 - t);
+  p.seed_lo = (uint32_t)(seed & 0xffffffffu), p.seed_hi = (uint32_t)(seed >> 32);
+  return map_launch_error(fa::launch_fwd_dropout(p, a->out_dtype, a->D, static_cast<hipStream_t>(stream)));
+}
+
 fa_status fa_fwd_varlen(const fa_fwd_varlen_args* a, void* stream) {
   const fa_status st = validate_fwd_varlen(a);
   if (st != FA_OK || a->total_q == 0 || a->max_seqlen_q == 0) return st;
@@ -290,7 +328,25 @@ size_t fa_bwd_workspace_bytes(const fa_bwd_args* a) {
   return fa::bwd_workspace_bytes(a->B, a->Hq, a->Nq, a->D);
 }
 
+namespace {
+fa_status bwd_impl(const fa_bwd_args* a, int drop_t, uint64_t seed, void* workspace, size_t ws_bytes,
+                   void* stream);
+}
+
 fa_status fa_bwd(const fa_bwd_args* a, void* workspace, size_t ws_bytes, void* stream) {
+  return bwd_impl(a, 0, 0, workspace, ws_bytes, stream);
+}
+
+fa_status fa_bwd_dropout(const fa_bwd_args* a, float p_drop, uint64_t seed, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  const int t = dropout_threshold(p_drop);
+  if (a && t < 0) return FA_ERR_ARG;
+  return bwd_impl(a, t < 0 ? 0 : t, seed, workspace, ws_bytes, stream);
+}
+
+namespace {
+fa_status bwd_impl(const fa_bwd_args* a, int drop_t, uint64_t seed, void* workspace, size_t ws_bytes,
+                   void* stream) {
   const fa_status st = validate_bwd(a);
   if (st != FA_OK) return st;
   if (a->Nq == 0 && a->Nk == 0) return FA_OK;
@@ -320,9 +376,13 @@ fa_status fa_bwd(const fa_bwd_args* a, void* workspace, size_t ws_bytes, void* s
   p.scale = a->scale;
   p.scale_log2 = a->scale * 1.4426950408889634f;
   p.causal = a->causal;
+  p.drop_t = (uint32_t)drop_t;
+  p.drop_scale = drop_t > 0 ? 256.f / (float)(256 - drop_t) : 1.f;
+  p.seed_lo = (uint32_t)(seed & 0xffffffffu), p.seed_hi = (uint32_t)(seed >> 32);
   fa::bwd_bind_workspace(p, workspace, a->D);
   return map_launch_error(fa::launch_bwd(p, a->D, static_cast<hipStream_t>(stream)));
 }
+}  // namespace
 
 size_t fa_decode_workspace_bytes(const fa_decode_args* a) {
   if (validate_decode(a) != FA_OK) return 0;

@@ -110,12 +110,14 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
   }
 }
 
-template <int D>
+template <int D, bool DROP = false>
 __global__ void __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_kv_kernel(BwdParams p) {
   using T = BwdTile<D>;
   constexpr int BC = kBwdBC, BR = kBwdBR, NW = kBwdWaves, NS = kBwdSlots;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[T::LDS_BYTES];
+  // dropout: per wave a 32 x 64 byte table of the tile's mask, [key][query]
+  constexpr int ZBYTES = DROP ? NW * 32 * BR : 0;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[T::LDS_BYTES + ZBYTES];
   unsigned char* ring = lds;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -277,8 +279,33 @@ bwd_kv_kernel(BwdParams p) {
       }
     }
 
+    // dropout mask of this wave's 32 keys and the tile's 64 queries: lane L draws the
+    // two 16-key groups of query q0 + L (the forward's words), spreads the 32 bytes into
+    // the wave's [key][query] table, and reads back the 4-query words of its own key
+    uint32_t zq[2][4] = {};
+    if constexpr (DROP) {
+      const int hq = hkv * p.G + (it % p.G);
+      unsigned char* zt = lds + T::LDS_BYTES + wave * 32 * BR;
+      const int chunk = (k0 + 32 * wave) / 32;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const u32x4_t w = dropout_words(chunk, h2, q0 + lane, hq, b, p.seed_lo, p.seed_hi);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            zt[(4 * h2 + 8 * a + e) * BR + lane] = (unsigned char)((w[a] >> (8 * e)) & 0xffu);
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+          zq[qb][rg] = *reinterpret_cast<const uint32_t*>(zt + l32 * BR + 32 * qb + 8 * rg + 4 * hi);
+    }
+
     // (2) P = exp(S - LSE), dS = P (dP - D_i); zero where the pair does not exist.  Two
-    //     instances: tiles that cross no edge run without any per-element test.
+    //     instances: tiles that cross no edge run without any per-element test.  With
+    //     dropout, dV takes the kept P / keep and dP is masked and scaled the same way.
     const bool edge = (k0 + BC > lk) || (q0 + BR > p.Nq) || (p.causal && k0 + BC - 1 > q0 + diag);
     auto probs = [&](auto masked) {
       constexpr bool M = decltype(masked)::value;
@@ -299,8 +326,14 @@ bwd_kv_kernel(BwdParams p) {
               const int lastk = min(lk - 1, p.causal ? q + diag : lk - 1);  // last key q sees
               pv = ((q < p.Nq) & (kw <= lastk)) ? pv : 0.f;
             }
-            s[qb][4 * rg + e] = pv;
-            dp[qb][4 * rg + e] = pv * (dp[qb][4 * rg + e] - dd[e]);
+            if constexpr (DROP) {
+              const float zs = dropout_keep(zq[qb][rg], e, p.drop_t) ? p.drop_scale : 0.f;
+              s[qb][4 * rg + e] = pv * zs;
+              dp[qb][4 * rg + e] = pv * (dp[qb][4 * rg + e] * zs - dd[e]);
+            } else {
+              s[qb][4 * rg + e] = pv;
+              dp[qb][4 * rg + e] = pv * (dp[qb][4 * rg + e] - dd[e]);
+            }
           }
         }
     };
@@ -418,7 +451,7 @@ struct DqTile {
 };
 
 // NW waves (32 query rows each) per workgroup; NS-slot ring (NS - 1 blocks ahead).
-template <int D, int NW, int NS>
+template <int D, int NW, int NS, bool DROP = false>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_q_kernel(BwdParams p) {
   using T = DqTile<D, NW, NS>;
@@ -575,6 +608,12 @@ bwd_q_kernel(BwdParams p) {
     const bool edge = (key0 + BC > lk) || (p.causal && key0 + BC - 1 > q_wg0 + diag);
     const int last = p.causal ? min(lk - 1, qi + diag) : lk - 1;
     u32x4_t pf[4];
+    // dropout: the forward's mask words of this lane's query for the block's two halves
+    u32x4_t zw[2] = {};
+    if constexpr (DROP) {
+      zw[0] = dropout_words(key0 / 32, hi, qi, hq, b, p.seed_lo, p.seed_hi);
+      zw[1] = dropout_words(key0 / 32 + 1, hi, qi, hq, b, p.seed_lo, p.seed_hi);
+    }
     auto grads = [&](auto masked) {  // two instances: blocks crossing no edge test nothing
       constexpr bool M = decltype(masked)::value;
 #pragma unroll
@@ -585,7 +624,10 @@ bwd_q_kernel(BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const float pv = fast_exp2(fmaf(s[h][r + e], c, -l2));
-            float ds = pv * (dp[h][r + e] - dd);
+            float dpz = dp[h][r + e];
+            if constexpr (DROP)
+              dpz = dropout_keep(zw[h][(r + e) >> 2], (r + e) & 3, p.drop_t) ? dpz * p.drop_scale : 0.f;
+            float ds = pv * (dpz - dd);
             if constexpr (M) {
               const int key = key0 + 32 * h + 8 * ((r + e) >> 2) + 4 * hi + ((r + e) & 3);
               ds = key > last ? 0.f : ds;
@@ -656,20 +698,20 @@ hipError_t launch(K kernel, int64_t grid, int block, const BwdParams& p, hipStre
                          args, 0, stream);
 }
 
-template <int D>
+template <int D, bool DROP>
 hipError_t launch_all(BwdParams p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
   constexpr int RPB = 256 / (D / 8);
   hipError_t e = launch(bwd_pre_kernel<D>, (rows + RPB - 1) / RPB, 256, p, stream);
   if (e != hipSuccess) return e;
   p.nkt = (p.Nk + kBwdBC - 1) / kBwdBC;
-  e = launch(bwd_kv_kernel<D>, (int64_t)p.nkt * p.Hkv * p.B, 64 * kBwdWaves, p, stream);
+  e = launch(bwd_kv_kernel<D, DROP>, (int64_t)p.nkt * p.Hkv * p.B, 64 * kBwdWaves, p, stream);
   if (e != hipSuccess) return e;
   // 128-row query tiles, two workgroups per compute unit: finer causal load balance than
   // 256-row tiles at these grid sizes (measured 0.91 -> 0.80 ms for B2 H16 N4096 D128)
   constexpr int NW = 4, NS = 2;
   const int64_t nqt = (p.Nq + 32 * NW - 1) / (32 * NW);
-  return launch(bwd_q_kernel<D, NW, NS>, nqt * p.Hq * p.B, 64 * NW, p, stream);
+  return launch(bwd_q_kernel<D, NW, NS, DROP>, nqt * p.Hq * p.B, 64 * NW, p, stream);
 }
 
 }  // namespace
@@ -685,7 +727,9 @@ void bwd_bind_workspace(BwdParams& p, void* workspace, int D) {
 }
 
 hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t stream) {
-  return D == 128 ? launch_all<128>(p, stream) : launch_all<64>(p, stream);
+  if (p.drop_t > 0)
+    return D == 128 ? launch_all<128, true>(p, stream) : launch_all<64, true>(p, stream);
+  return D == 128 ? launch_all<128, false>(p, stream) : launch_all<64, false>(p, stream);
 }
 
 }  // namespace fa

@@ -128,6 +128,35 @@ __device__ __forceinline__ void wait_vmcnt() {
   else if constexpr (N == 9) FA_WAIT_VMCNT(9);
   else FA_WAIT_VMCNT(16);
 }
+// Philox4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
+// as easy as 1, 2, 3", SC 2011): four 32-bit words from a 4-word counter and a 2-word key.
+__device__ __forceinline__ u32x4_t philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4_t{c0, c1, c2, c3};
+}
+
+// Dropout mask words of one query row and one group of 16 keys: the keys
+// 32 c + 4 h2 + 8 a + e (a, e = 0..3) of query i, head h, batch entry b take byte 4 a + e
+// of philox(2 c + h2, i, h, b; seed).  Byte n sits at bits 8 (n % 4) of word n / 4.
+__device__ __forceinline__ u32x4_t dropout_words(int chunk, int h2, int i, int h, int b,
+                                                 uint32_t seed_lo, uint32_t seed_hi) {
+  return philox4x32_10((uint32_t)(2 * chunk + h2), (uint32_t)i, (uint32_t)h, (uint32_t)b, seed_lo, seed_hi);
+}
+__device__ __forceinline__ bool dropout_keep(uint32_t word, int byte, uint32_t threshold) {
+  return ((word >> (8 * byte)) & 0xffu) >= threshold;
+}
+
 // Workgroup barrier without the memory fence __syncthreads() adds (which waits for every
 // outstanding load, ring prefetches included).  Callers order LDS themselves: each wave
 // waits for its own ring loads (FA_WAIT_VMCNT) and LDS reads (lgkmcnt) before it.

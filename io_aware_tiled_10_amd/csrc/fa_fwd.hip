@@ -95,11 +95,12 @@ struct Slot {
 // LSE = m*scale + ln(l) use the same reference, so the result does not depend on it.
 constexpr float kMaxBlockSum = 256.f;
 
-template <int D, bool OUT_F32, bool QK8>
+template <int D, bool OUT_F32, bool QK8, bool DROP = false>
 __global__ void __launch_bounds__(64 * kFwdWaves) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_bf16_kernel(FwdParams p) {
   using T = FwdTile<D, QK8>;
   static_assert(!QK8 || D == 128, "the E4M3 path is built for D = 128");
+  static_assert(!(QK8 && DROP), "dropout is built for the bf16 path");
   constexpr int BR = kFwdBR, BC = kFwdBC, NW = kFwdWaves, NS = kFwdSlots;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[T::LDS_BYTES];
   unsigned char* kring = lds;
@@ -309,6 +310,14 @@ fwd_bf16_kernel(FwdParams p) {
     // probabilities against the current reference, packed to bf16 as the B operand of
     // the second product; returns this lane's sum of them
     u32x4_t pf[4];
+    // dropout: the mask bytes of this lane's 16 keys of each half (register r <-> byte
+    // r); the sum l keeps every probability, P V only the kept ones (the 1 / keep factor
+    // is applied with 1 / l at the end)
+    u32x4_t zw0{}, zw1{};
+    if constexpr (DROP) {
+      zw0 = dropout_words(key0 / 32, hi, qi, hq, b, p.seed_lo, p.seed_hi);
+      zw1 = dropout_words(key0 / 32 + 1, hi, qi, hq, b, p.seed_lo, p.seed_hi);
+    }
     auto probs = [&](const f32x16_t& a0, const f32x16_t& a1) {
       const float mc = (m == -INFINITY ? 0.f : m) * c;
       float rs = 0.f;
@@ -317,8 +326,18 @@ fwd_bf16_kernel(FwdParams p) {
         const float p0 = fast_exp2(fmaf(a0[r], cb, -mc)), p1 = fast_exp2(fmaf(a0[r + 1], cb, -mc));
         const float p2 = fast_exp2(fmaf(a1[r], cb, -mc)), p3 = fast_exp2(fmaf(a1[r + 1], cb, -mc));
         rs += (p0 + p1) + (p2 + p3);
-        pf[r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
-        pf[2 + (r >> 3)][(r & 7) >> 1] = pack_bf16(p2, p3);
+        if constexpr (DROP) {
+          const uint32_t t = p.drop_t;
+          pf[r >> 3][(r & 7) >> 1] =
+              pack_bf16(dropout_keep(zw0[r >> 2], r & 3, t) ? p0 : 0.f,
+                        dropout_keep(zw0[(r + 1) >> 2], (r + 1) & 3, t) ? p1 : 0.f);
+          pf[2 + (r >> 3)][(r & 7) >> 1] =
+              pack_bf16(dropout_keep(zw1[r >> 2], r & 3, t) ? p2 : 0.f,
+                        dropout_keep(zw1[(r + 1) >> 2], (r + 1) & 3, t) ? p3 : 0.f);
+        } else {
+          pf[r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
+          pf[2 + (r >> 3)][(r & 7) >> 1] = pack_bf16(p2, p3);
+        }
       }
       return rs;
     };
@@ -396,9 +415,9 @@ fwd_bf16_kernel(FwdParams p) {
   if (j + 1 < nblk) step(j + 1, Slot<1>{}, sb0, sb1, sa0, sa1);
   if (j + 2 < nblk) step(j + 2, Slot<2>{}, sa0, sa1, sb0, sb1);
 
-  // ---- epilogue: O = acc / l once; LSE = m * scale + ln(l)
+  // ---- epilogue: O = acc / l once (times 1 / keep with dropout); LSE = m * scale + ln(l)
   const float lt = halves_sum(l);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float inv = lt > 0.f ? (DROP ? p.drop_scale : 1.f) / lt : 0.f;
   if (qi < nq) {
     const int64_t orow0 = b * p.os0 + hq * p.os1 + (qr0 + qi) * p.os2;
     if constexpr (OUT_F32) {
@@ -555,6 +574,19 @@ hipError_t launch_fwd(const FwdParams& p0, int in_dtype, int out_dtype, int D, h
                 : launch(fwd_bf16_kernel<128, false, false>, (int)grid, 64 * kFwdWaves, p, stream);
   return of32 ? launch(fwd_bf16_kernel<64, true, false>, (int)grid, 64 * kFwdWaves, p, stream)
               : launch(fwd_bf16_kernel<64, false, false>, (int)grid, 64 * kFwdWaves, p, stream);
+}
+
+hipError_t launch_fwd_dropout(const FwdParams& p0, int out_dtype, int D, hipStream_t stream) {
+  FwdParams p = p0;
+  p.nqt = (p.Nq + kFwdBR - 1) / kFwdBR;
+  const int64_t grid = (int64_t)p.nqt * p.Hq * p.B;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const bool of32 = out_dtype == FA_F32;
+  if (D == 128)
+    return of32 ? launch(fwd_bf16_kernel<128, true, false, true>, (int)grid, 64 * kFwdWaves, p, stream)
+                : launch(fwd_bf16_kernel<128, false, false, true>, (int)grid, 64 * kFwdWaves, p, stream);
+  return of32 ? launch(fwd_bf16_kernel<64, true, false, true>, (int)grid, 64 * kFwdWaves, p, stream)
+              : launch(fwd_bf16_kernel<64, false, false, true>, (int)grid, 64 * kFwdWaves, p, stream);
 }
 
 hipError_t launch_fwd_fp8(const FwdParams& p0, int out_dtype, hipStream_t stream) {

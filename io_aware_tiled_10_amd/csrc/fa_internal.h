@@ -26,12 +26,18 @@ struct FwdParams {
   const float* q_scale;
   const float* k_scale;
   int64_t qsc_b, qsc_h, ksc_b, ksc_h;
+  // dropout on P (when drop_t > 0): keep iff the Philox byte >= drop_t, scale kept values
+  // by drop_scale = 256 / (256 - drop_t)
+  uint32_t drop_t, seed_lo, seed_hi;
+  float drop_scale;
   int B, Hq, Hkv, Nq, Nk, G, nqt;  // packed batches: Nq = longest sequence
   float scale, scale_log2;
   int causal;
 };
 
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int out_dtype, int D, hipStream_t stream);
+// bf16 forward with dropout on P (p.drop_t > 0, p.seed_*, p.drop_scale).
+hipError_t launch_fwd_dropout(const FwdParams& p, int out_dtype, int D, hipStream_t stream);
 // Q and K as E4M3 codes with per-64-row steps, V bf16 (D = 128).
 hipError_t launch_fwd_fp8(const FwdParams& p, int out_dtype, hipStream_t stream);
 
@@ -57,6 +63,8 @@ struct BwdParams {
   int B, Hq, Hkv, Nq, Nk, G, nkt;
   float scale, scale_log2;
   int causal;
+  uint32_t drop_t, seed_lo, seed_hi;  // dropout as in the forward (drop_t == 0: none)
+  float drop_scale;
 };
 
 size_t bwd_workspace_bytes(int B, int Hq, int Nq, int D);

@@ -273,3 +273,18 @@ FP8_BAD = [({"D": 64}, UNSUP), ({"block": 128}, UNSUP), ({"Hq": 3, "Hkv": 2}, SH
 def test_fwd_fp8_rejects_bad_arguments(change, status):
     assert fb.lib().fa_fwd_fp8(ctypes.byref(good_fp8(**change)), None) == status
     assert fb.lib().fa_fwd_fp8(ctypes.byref(good_fp8(Nq=0)), None) == OK
+
+
+@pytest.mark.parametrize("p", [-0.1, 1.0, 1.5, float("nan")])
+def test_dropout_rejects_bad_probability(p):
+    assert fb.lib().fa_fwd_dropout(ctypes.byref(good_fwd()), p, 1, None) == ARG
+    assert fb.lib().fa_bwd_dropout(ctypes.byref(good_bwd()), p, 1, FAKE, 1 << 30, None) == ARG
+
+
+def test_dropout_rejects_fp32_and_bad_args_first():
+    a = good_fwd(in_dtype=fb.FA_F32, out_dtype=fb.FA_F32, D=64)
+    assert fb.lib().fa_fwd_dropout(ctypes.byref(a), 0.1, 1, None) == UNSUP
+    assert fb.lib().fa_fwd_dropout(ctypes.byref(good_fwd(D=96)), 0.1, 1, None) == UNSUP
+    assert fb.lib().fa_bwd_dropout(ctypes.byref(good_bwd(dtype=fb.FA_F32)), 0.1, 1, FAKE, 1 << 30, None) == DTYPE
+    assert fb.lib().fa_fwd_dropout(None, 0.1, 1, None) == NULL
+    assert fb.lib().fa_bwd_dropout(None, 0.1, 1, None, 0, None) == NULL
