@@ -362,7 +362,10 @@ def write_traffic_summary(fetch_csv: str, write_csv: str, out: str) -> None:
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"])
-            if "fwd_bf16_kernel<128, false>" in r["Kernel_Name"] and int(r["Grid_Size"]) == FWD_GRID_THREADS:
+            name = r["Kernel_Name"]
+            # the bf16 forward: out_dtype bf16, no E4M3, no dropout
+            if ("fwd_bf16_kernel<128, false, false, false>" in name
+                    and int(r["Grid_Size"]) == FWD_GRID_THREADS):
                 fwd.append(v)
             if "copyBuffer" in r["Kernel_Name"] and v > 0.25 * COPY_BYTES / 1024:
                 copy.append(v)
