@@ -27,6 +27,11 @@ bool strides_ok(const int64_t* st, int n, int elem_bytes) {
 
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
+// Row-to-row strides reach the kernels' 32-bit buffer offsets multiplied by up to 256
+// rows; 8 MiB per row keeps every such offset below 2^31.
+constexpr int64_t kMaxPitchBytes = int64_t(1) << 23;
+bool pitch_ok(int64_t stride_elems, int elem_bytes) { return stride_elems * elem_bytes <= kMaxPitchBytes; }
+
 fa_status map_launch_error(hipError_t e) {
   switch (e) {
     case hipSuccess:
@@ -63,6 +68,8 @@ fa_status validate_fwd(const fa_fwd_args* a) {
   if (!strides_ok(a->q_stride, 3, ib) || !strides_ok(a->k_stride, 3, ib) ||
       !strides_ok(a->v_stride, 3, ib) || !strides_ok(a->o_stride, 3, ob))
     return FA_ERR_STRIDE;
+  if (!pitch_ok(a->q_stride[2], ib) || !pitch_ok(a->k_stride[2], ib) || !pitch_ok(a->v_stride[2], ib))
+    return FA_ERR_SHAPE;
   if (a->lse && (reinterpret_cast<uintptr_t>(a->lse) & 3u)) return FA_ERR_STRIDE;
   return FA_OK;
 }
@@ -85,6 +92,8 @@ fa_status validate_bwd(const fa_bwd_args* a) {
                          a->do_stride, a->dq_stride, a->dk_stride, a->dv_stride};
   for (const int64_t* s : st)
     if (!strides_ok(s, 3, 2)) return FA_ERR_STRIDE;
+  for (const int64_t* s : st)
+    if (!pitch_ok(s[2], 2)) return FA_ERR_SHAPE;
   if (a->lse && (reinterpret_cast<uintptr_t>(a->lse) & 3u)) return FA_ERR_STRIDE;
   return FA_OK;
 }
@@ -109,6 +118,8 @@ fa_status validate_fwd_varlen(const fa_fwd_varlen_args* a) {
   if (!strides_ok(a->q_stride, 2, 2) || !strides_ok(a->k_stride, 2, 2) ||
       !strides_ok(a->v_stride, 2, 2) || !strides_ok(a->o_stride, 2, ob))
     return FA_ERR_STRIDE;
+  if (!pitch_ok(a->q_stride[0], 2) || !pitch_ok(a->k_stride[0], 2) || !pitch_ok(a->v_stride[0], 2))
+    return FA_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(a->cu_seqlens_q) & 3u) ||
       (reinterpret_cast<uintptr_t>(a->cu_seqlens_k) & 3u))
     return FA_ERR_STRIDE;
@@ -143,6 +154,8 @@ fa_status validate_decode(const fa_decode_args* a) {
   if (!strides_ok(a->q_stride, 2, 2) || !strides_ok(a->k_stride, 3, 2) ||
       !strides_ok(a->v_stride, 3, 2) || !strides_ok(a->o_stride, 2, ob))
     return FA_ERR_STRIDE;
+  if (!pitch_ok(a->q_stride[1], 2) || !pitch_ok(a->k_stride[2], 2) || !pitch_ok(a->v_stride[2], 2))
+    return FA_ERR_SHAPE;
   if (a->lse && (reinterpret_cast<uintptr_t>(a->lse) & 3u)) return FA_ERR_STRIDE;
   return FA_OK;
 }
@@ -157,6 +170,7 @@ fa_status validate_quantize(const fa_quantize_fp8_args* a) {
   if (!aligned16(a->x) || !aligned16(a->codes)) return FA_ERR_STRIDE;
   if (reinterpret_cast<uintptr_t>(a->scales) & 3u) return FA_ERR_STRIDE;
   if (!strides_ok(a->x_stride, 3, 2) || !strides_ok(a->codes_stride, 3, 1)) return FA_ERR_STRIDE;
+  if (!pitch_ok(a->x_stride[2], 2) || !pitch_ok(a->codes_stride[2], 1)) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -178,6 +192,8 @@ fa_status validate_fwd_fp8(const fa_fwd_fp8_args* a) {
   if (!strides_ok(a->q_stride, 3, 1) || !strides_ok(a->k_stride, 3, 1) ||
       !strides_ok(a->v_stride, 3, 2) || !strides_ok(a->o_stride, 3, ob))
     return FA_ERR_STRIDE;
+  if (!pitch_ok(a->q_stride[2], 1) || !pitch_ok(a->k_stride[2], 1) || !pitch_ok(a->v_stride[2], 2))
+    return FA_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(a->q_scales) & 3u) || (reinterpret_cast<uintptr_t>(a->k_scales) & 3u))
     return FA_ERR_STRIDE;
   if (a->lse && (reinterpret_cast<uintptr_t>(a->lse) & 3u)) return FA_ERR_STRIDE;
@@ -223,6 +239,8 @@ fa_status validate_decode_paged(const fa_decode_paged_args* a) {
       !strides_ok(a->v_stride, 3, 2) || !strides_ok(a->o_stride, 2, ob))
     return FA_ERR_STRIDE;
   if (reinterpret_cast<uintptr_t>(a->block_table) & 3u) return FA_ERR_STRIDE;
+  if (!pitch_ok(a->q_stride[1], 2) || !pitch_ok(a->k_stride[2], 2) || !pitch_ok(a->v_stride[2], 2))
+    return FA_ERR_SHAPE;
   // byte offsets inside one page are 32-bit
   if ((int64_t)a->page_size * a->k_stride[2] * 2 > 0x7fffffff ||
       (int64_t)a->page_size * a->v_stride[2] * 2 > 0x7fffffff)

@@ -288,3 +288,13 @@ def test_dropout_rejects_fp32_and_bad_args_first():
     assert fb.lib().fa_bwd_dropout(ctypes.byref(good_bwd(dtype=fb.FA_F32)), 0.1, 1, FAKE, 1 << 30, None) == DTYPE
     assert fb.lib().fa_fwd_dropout(None, 0.1, 1, None) == NULL
     assert fb.lib().fa_bwd_dropout(None, 0.1, 1, None, 0, None) == NULL
+
+
+def test_row_pitches_beyond_8_mib_are_rejected():
+    big = (1 << 22) + 8  # elements: bf16 rows of just over 8 MiB
+    assert fb.lib().fa_fwd(ctypes.byref(good_fwd(k_stride=fb.c_i64x3(0, 0, big))), None) == SHAPE
+    st = fb.c_i64x3(0, 0, big)
+    assert fb.lib().fa_bwd(ctypes.byref(good_bwd(dq_stride=st)), FAKE, 1 << 30, None) == SHAPE
+    assert fb.lib().fa_decode(ctypes.byref(good_dec(v_stride=fb.c_i64x3(0, 0, big))), FAKE, 1 << 30, None) == SHAPE
+    assert fb.lib().fa_fwd_varlen(ctypes.byref(good_varlen(q_stride=fb.c_i64x2(big, 128))), None) == SHAPE
+    assert fb.lib().fa_quantize_fp8(ctypes.byref(good_quant(x_stride=fb.c_i64x3(0, 0, big))), None) == SHAPE
