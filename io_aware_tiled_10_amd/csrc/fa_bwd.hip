@@ -124,11 +124,12 @@ bwd_kv_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
-  int t = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int kt = t % p.nkt;  // causal: low key tiles (most query tiles) first
-  t /= p.nkt;
-  const int hkv = t % p.Hkv;
-  const int b = t / p.Hkv;
+  // tile: each XCD holds whole (batch entry, KV head) groups; inside, key tiles in rank
+  // order, so the heaviest (causal: low key tiles see the most query tiles) go first
+  const TileId tix = tile_order(blockIdx.x, gridDim.x, p.B * p.Hkv, p.nkt, 1);
+  const int kt = tix.rank;
+  const int hkv = tix.pair % p.Hkv;
+  const int b = tix.pair / p.Hkv;
 
   int lk = p.Nk;
   if (p.kv_lens) {
@@ -464,15 +465,12 @@ bwd_q_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // tile: XCD-contiguous, KV-head-major, heavy causal tiles first (as the forward)
-  int t = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int gi = t % p.G;
-  t /= p.G;
+  // tile: ordered as the forward's (heavy causal tiles first inside each XCD's groups)
   const int nqt = (p.Nq + BR - 1) / BR;
-  const int rank = t % nqt;
-  t /= nqt;
-  const int hkv = t % p.Hkv;
-  const int b = t / p.Hkv;
+  const TileId tix = tile_order(blockIdx.x, gridDim.x, p.B * p.Hkv, nqt, p.G);
+  const int gi = tix.gi, rank = tix.rank;
+  const int hkv = tix.pair % p.Hkv;
+  const int b = tix.pair / p.Hkv;
   const int qt = p.causal ? nqt - 1 - rank : rank;
   const int hq = hkv * p.G + gi;
 

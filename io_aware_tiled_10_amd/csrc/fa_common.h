@@ -75,6 +75,37 @@ __device__ __forceinline__ int xcd_contiguous(int id, int total) {
   return x * q + (x < r ? x : r) + k;
 }
 
+// Tile order for a grid of npair groups (batch entry, KV head) x nrank ranks x ng heads
+// (total = npair * nrank * ng).  Each XCD receives a contiguous range of whole groups, so
+// the tiles that share a group's K/V share that XCD's L2.  When the groups split evenly
+// over the XCDs, the rank varies slowest inside each XCD's range: every XCD dispatches
+// the rank-0 tiles of all its groups first, then rank 1, ..., which with rank 0 the
+// heaviest gives a longest-first schedule.  Otherwise (or without rank_major) ranks vary
+// right after the heads.
+struct TileId {
+  int gi, rank, pair;
+};
+__device__ __forceinline__ TileId tile_order(int id, int total, int npair, int nrank, int ng,
+                                             bool rank_major = true) {
+  const int t = xcd_contiguous(id, total);
+  TileId r;
+  if (rank_major && npair % kNumXcd == 0) {
+    const int per = npair / kNumXcd, span = per * nrank * ng;
+    const int x = t / span;
+    int u = t - x * span;
+    r.gi = u % ng;
+    u /= ng;
+    r.rank = u / per;
+    r.pair = x * per + u % per;
+  } else {
+    r.gi = t % ng;
+    const int u = t / ng;
+    r.rank = u % nrank;
+    r.pair = u / nrank;
+  }
+  return r;
+}
+
 __device__ __forceinline__ const uint16_t* as_u16(const void* p) {
   return static_cast<const uint16_t*>(p);
 }

@@ -110,17 +110,15 @@ fwd_bf16_kernel(FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // ---- which tile: XCD-contiguous, heavy causal tiles first.  The tiles of one (batch
-  // entry, KV head) are consecutive, so they share an XCD's L2; the KV head varies
-  // slowest, so every XCD receives every batch entry and sequences of different length
-  // (packed batches) spread evenly over the XCDs.
-  int t = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int gi = t % p.G;
-  t /= p.G;
-  const int rank = t % p.nqt;
-  t /= p.nqt;
-  const int b = t % p.B;
-  const int hkv = t / p.B;
+  // ---- which tile: the (batch entry, KV head) groups of each XCD share its L2, heavy
+  // causal tiles (rank 0) go first; the KV head varies slowest over the groups, so every
+  // XCD receives every batch entry and sequences of different length (packed batches)
+  // spread evenly over the XCDs.  Packed batches keep each group's ranks together: their
+  // rank-0 tiles are empty for all but the longest sequences.
+  const TileId tid8 = tile_order(blockIdx.x, gridDim.x, p.B * p.Hkv, p.nqt, p.G, p.cu_q == nullptr);
+  const int gi = tid8.gi, rank = tid8.rank;
+  const int b = tid8.pair % p.B;
+  const int hkv = tid8.pair / p.B;
   const int qt = p.causal ? p.nqt - 1 - rank : rank;
   const int hq = hkv * p.G + gi;
 
