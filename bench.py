@@ -284,8 +284,16 @@ def cpu_baseline(budget_s: float = 12.0):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    cpu_model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu_model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
     return {"value": round(per_head * done / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model,
             "sample": f"fp64 numpy oracle forward on {done} whole query head(s) of the B1 Hq32 Hkv8 N16384 "
                       f"D128 causal workload ({done * per_head / 1e9:.1f} GFLOP credited, {el:.1f} s)"}
 
@@ -475,7 +483,10 @@ def main():
         ms = leg_ms[n]
         tf = leg.flops / (ms * 1e-3) / 1e12
         flops += leg.flops
-        rec = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        per_step = sorted(a.elapsed_time(b) for a, b in ev[n])
+        rec = {"ms": round(ms, 4), "median_ms": round(float(np.median(per_step)), 4),
+               "min_ms": round(per_step[0], 4), "tflops": round(tf, 2),
+               "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
         if n == "decode":
             gbs = leg.bytes / (ms * 1e-3) / 1e9
             rec.update({"hbm_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
@@ -569,6 +580,9 @@ def main():
     }
     if ceil is not None:
         line["ceilings"] = ceil
+    props = torch.cuda.get_device_properties(0)
+    line["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                      "hip_runtime": getattr(torch.version, "hip", None), "cus": props.multi_processor_count}
     print(json.dumps(line), flush=True)
 
 
