@@ -25,8 +25,9 @@ Throughput counts only matmul FLOPs over the (query, key) pairs that exist:
 backward (five products, one of them the recompute of S).  Decode bandwidth counts
 each valid cached K/V byte once plus q and O.
 
-Prints one JSON line.  The CPU baseline times the fp64 oracle forward on a bounded
-sample (whole query heads of the forward workload) on the host cores.  `roofline`
+Prints one JSON line.  The CPU baseline times the fp64 oracle on bounded samples of
+each leg's workload (whole query heads, (batch, head) slices, sequences) on the host
+cores and reports the step-level rate those samples imply.  `roofline`
 describes the forward kernel (the largest share of the step): achieved = credited
 FLOPs / mean HIP-event duration of its launch; `traffic` = HBM bytes per launch from
 the committed counter summary (FETCH_SIZE and WRITE_SIZE scaled by their readings
@@ -261,24 +262,10 @@ def time_aux(leg, stream, reps=20):
 
 
 # ------------------------------------------------------------------------------------
-# CPU baseline: the oracle as it stands, on whole query heads of the forward workload
+# CPU baseline: the oracle as it stands, on bounded samples of each leg's workload
 # ------------------------------------------------------------------------------------
 
-def cpu_baseline(budget_s: float = 12.0):
-    import oracle
-
-    cfg = FWD_CFG
-    x = inputs.attention_inputs(1, cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["N"], cfg["D"], "bf16", 0)
-    G = cfg["Hq"] // cfg["Hkv"]
-    per_head = 4 * cfg["D"] * pairs(cfg["N"], cfg["N"], cfg["causal"])
-    done, t0 = 0, time.perf_counter()
-    while done < cfg["Hq"]:
-        h = done
-        oracle.attn_fwd(x.q[:, h:h + 1], x.k[:, h // G:h // G + 1], x.v[:, h // G:h // G + 1], None, True)
-        done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    el = time.perf_counter() - t0
+def _host_threads_and_model():
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -292,10 +279,78 @@ def cpu_baseline(budget_s: float = 12.0):
                 break
     except OSError:  # pragma: no cover
         pass
-    return {"value": round(per_head * done / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "cpu_model": cpu_model,
-            "sample": f"fp64 numpy oracle forward on {done} whole query head(s) of the B1 Hq32 Hkv8 N16384 "
-                      f"D128 causal workload ({done * per_head / 1e9:.1f} GFLOP credited, {el:.1f} s)"}
+    return int(threads), cpu_model
+
+
+def cpu_baseline(budgets=(9.0, 4.0, 3.0)):
+    """The fp64 oracle timed on the host cores, leg by leg, on bounded samples of the
+    step's own workloads: whole query heads of the forward, whole (batch, head) slices
+    of the backward, whole sequences of the decode (each until its time budget in
+    seconds runs out; input generation is not timed).  `value` is the step's credited
+    FLOPs over the time the oracle would take for the whole step at those rates."""
+    import oracle
+
+    rates, samples = {}, {}
+    # forward: query heads of B1 Hq32 Hkv8 N16384 D128 causal
+    cfg = FWD_CFG
+    x = inputs.attention_inputs(1, cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["N"], cfg["D"], "bf16", 0)
+    G = cfg["Hq"] // cfg["Hkv"]
+    per_head = 4 * cfg["D"] * pairs(cfg["N"], cfg["N"], cfg["causal"])
+    step_flops = {"fwd": per_head * cfg["Hq"]}
+    done, t0 = 0, time.perf_counter()
+    while done < cfg["Hq"]:
+        h = done
+        oracle.attn_fwd(x.q[:, h:h + 1], x.k[:, h // G:h // G + 1], x.v[:, h // G:h // G + 1], None, True)
+        done += 1
+        if time.perf_counter() - t0 >= budgets[0]:
+            break
+    el = time.perf_counter() - t0
+    rates["fwd"] = per_head * done / el
+    samples["fwd"] = f"{done} of 32 query heads ({done * per_head / 1e9:.1f} GFLOP, {el:.1f} s)"
+    del x
+    # backward: (batch, head) slices of B2 H16 N4096 D128 causal
+    cfg = BWD_CFG
+    B, H, N, D = cfg["B"], cfg["H"], cfg["N"], cfg["D"]
+    x = inputs.attention_inputs(B, H, H, N, N, D, "bf16", 0, with_grad=True)
+    per_head = 10 * D * pairs(N, N, cfg["causal"])
+    step_flops["bwd"] = per_head * B * H
+    done, t0 = 0, time.perf_counter()
+    while done < B * H:
+        b, h = divmod(done, H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.attn_bwd(x.q[sl], x.k[sl], x.v[sl], x.do[sl], None, True)
+        done += 1
+        if time.perf_counter() - t0 >= budgets[1]:
+            break
+    el = time.perf_counter() - t0
+    rates["bwd"] = per_head * done / el
+    samples["bwd"] = f"{done} of {B * H} (batch, head) slices ({done * per_head / 1e9:.1f} GFLOP, {el:.1f} s)"
+    del x
+    # decode: whole sequences of the 64-sequence workload
+    cfg = DEC_CFG
+    d = inputs.decode_inputs(cfg["Bs"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["lo"], cfg["hi"], 0)
+    fl_per_key = 4 * cfg["D"] * cfg["Hq"]
+    step_flops["decode"] = fl_per_key * int(d.seq_lens.sum())
+    done, keys, el = 0, 0, 0.0
+    while done < cfg["Bs"] and el < budgets[2]:
+        k, v = d.kv(done)
+        L = int(d.seq_lens[done])
+        t0 = time.perf_counter()
+        oracle.attn_decode(d.q[done:done + 1], k[None], v[None], [L])
+        el += time.perf_counter() - t0
+        done, keys = done + 1, keys + L
+    rates["decode"] = fl_per_key * keys / el
+    samples["decode"] = (f"{done} of 64 sequences ({keys} cached positions, "
+                         f"{2 * cfg['Hkv'] * cfg['D'] * 2 * keys / el / 1e9:.2f} GB/s of K/V, {el:.1f} s)")
+
+    threads, cpu_model = _host_threads_and_model()
+    t_step = sum(step_flops[k] / rates[k] for k in step_flops)
+    return {"value": round(sum(step_flops.values()) / t_step / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle", "cpu_model": cpu_model,
+            "legs_tflops": {k: round(r / 1e12, 6) for k, r in rates.items()},
+            "est_s_per_step": round(t_step, 1),
+            "sample": "fp64 numpy oracle on the step's workloads, timed per leg on bounded samples: "
+                      + "; ".join(f"{k}: {v}" for k, v in samples.items())}
 
 
 def ceilings():
@@ -412,7 +467,8 @@ def write_traffic_summary(fetch_csv: str, write_csv: str, out: str) -> None:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=64,
+                    help="timed steps (64 steps of the default legs take about 0.2 s)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="fwd,bwd,decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
