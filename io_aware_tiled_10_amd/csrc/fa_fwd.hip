@@ -44,6 +44,8 @@
 //    accumulation (half the bf16 product's time), K blocks are staged at one byte per
 //    element, and the two blocks' steps fold into the exp2 coefficient of each block, so
 //    the softmax, P V and the epilogue are those of the bf16 path.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -273,8 +275,10 @@ fwd_bf16_kernel(FwdParams p) {
   // One block: (s0, s1) hold the scores of block j (keys 64 j + [0, 32), + [32, 64));
   // the scores of block j + 1 are produced into (n0, n1).
   // `slot` is j % NS.
-  auto step = [&](int j, auto slot, f32x16_t& s0, f32x16_t& s1, f32x16_t& n0, f32x16_t& n1) {
+  auto step = [&](int j, auto slot, f32x16_t& s0, f32x16_t& s1, f32x16_t& n0, f32x16_t& n1,
+                  auto first) {
     constexpr int sl = decltype(slot)::value;
+    constexpr bool kFirst = decltype(first)::value;
     constexpr uint32_t vo = sl * T::TBYTES;
     // K_{j+3} and V_{j+2} into the slots of K_{j-1} and V_{j-2}, which are free
     dma_k(j + 3, (sl + 3) % NS);
@@ -345,7 +349,7 @@ fwd_bf16_kernel(FwdParams p) {
     // there is no reference yet -- the scores are recomputed from the K block still in
     // its slot, the reference moves to the row maximum, and the running sum and the
     // accumulator are rescaled.  The test also catches inf and NaN sums.
-    if (j == 0 || __builtin_amdgcn_ballot_w64(!(rs <= kMaxBlockSum))) {
+    if (kFirst || __builtin_amdgcn_ballot_w64(!(rs <= kMaxBlockSum))) {
       asm volatile("" ::: "memory");  // keep this path's LDS reads off the common path
       qk(sl, s0, s1);
       mask(s0, s1);
@@ -400,18 +404,22 @@ fwd_bf16_kernel(FwdParams p) {
   FA_WAIT_LGKMCNT0();  // K slot 0 is refilled at the top of the first block:
   __syncthreads();     // every wave's reads of it must be done
 
-  // NS blocks per trip, so every slot index is a constant; the score registers alternate
+  // The first block (which sets the reference) is peeled off, so the loop body carries
+  // no test of j and its exps can be scheduled between the next block's MFMAs.  NS
+  // blocks per trip, so every slot index is a constant; the score registers alternate.
   static_assert(NS == 4, "the unrolled loop below walks four slots");
-  int j = 0;
+  using Later = std::false_type;
+  step(0, Slot<0>{}, sa0, sa1, sb0, sb1, std::true_type{});
+  int j = 1;
   for (; j + 3 < nblk; j += 4) {
-    step(j, Slot<0>{}, sa0, sa1, sb0, sb1);
-    step(j + 1, Slot<1>{}, sb0, sb1, sa0, sa1);
-    step(j + 2, Slot<2>{}, sa0, sa1, sb0, sb1);
-    step(j + 3, Slot<3>{}, sb0, sb1, sa0, sa1);
+    step(j, Slot<1>{}, sb0, sb1, sa0, sa1, Later{});
+    step(j + 1, Slot<2>{}, sa0, sa1, sb0, sb1, Later{});
+    step(j + 2, Slot<3>{}, sb0, sb1, sa0, sa1, Later{});
+    step(j + 3, Slot<0>{}, sa0, sa1, sb0, sb1, Later{});
   }
-  if (j < nblk) step(j, Slot<0>{}, sa0, sa1, sb0, sb1);
-  if (j + 1 < nblk) step(j + 1, Slot<1>{}, sb0, sb1, sa0, sa1);
-  if (j + 2 < nblk) step(j + 2, Slot<2>{}, sa0, sa1, sb0, sb1);
+  if (j < nblk) step(j, Slot<1>{}, sb0, sb1, sa0, sa1, Later{});
+  if (j + 1 < nblk) step(j + 1, Slot<2>{}, sa0, sa1, sb0, sb1, Later{});
+  if (j + 2 < nblk) step(j + 2, Slot<3>{}, sb0, sb1, sa0, sa1, Later{});
 
   // ---- epilogue: O = acc / l once (times 1 / keep with dropout); LSE = m * scale + ln(l)
   const float lt = halves_sum(l);
