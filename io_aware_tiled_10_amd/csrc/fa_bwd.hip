@@ -12,15 +12,15 @@
 // written once, so the backward is deterministic):
 //  1. bwd_pre: per query row, D_i = rowsum(dO * O) in fp32 and LSE * log2(e), stored
 //     side by side;
-//  2. bwd_kv: one workgroup (4 waves) per 128-key tile of a KV head.  Each wave keeps
-//     its 32 keys' K and V rows (operands of S and dP) and the fp32 dK, dV accumulators
-//     in registers, and walks the 64-row query tiles of every query head of the GQA
-//     group that can see the tile (causal: from the diagonal down).  Q, dO and the row
-//     statistics of each tile stream from L2/HBM straight into a three-slot LDS ring
-//     (LDS DMA, XOR-swizzled 16-byte slots), two tiles ahead.  Per tile: S = Q K^T and
-//     dP = dO V^T on 32x32x16 bf16 MFMA (one lane per key, so P and dS are already the
-//     A operands of dV += P^T dO and dK += dS^T Q), with dO^T and Q^T from transposing
-//     LDS reads;
+//  2. bwd_kv: one workgroup (8 waves) per 128-key tile of a KV head, walking the 64-row
+//     query tiles of every query head of the GQA group that can see the tile (causal:
+//     from the diagonal down).  Q, dO and the row statistics of each tile stream from
+//     L2/HBM straight into a three-slot LDS ring (LDS DMA, XOR-swizzled 16-byte slots),
+//     two tiles ahead.  Each 32-key group is served by two waves: one keeps the keys' K
+//     rows and forms S = Q K^T, P and dV += P^T dO; the other keeps their V rows and
+//     forms dP = dO V^T, dS = P (dP - D_i) (P read from LDS) and dK += dS^T Q.  On
+//     32x32x16 bf16 MFMA with one lane per key, P and dS are already the A operands of
+//     the second products, whose dO^T and Q^T come from transposing LDS reads;
 //  3. bwd_q: the forward's layout turned to dQ.  One workgroup (4 waves) per 128-row
 //     query tile, two per compute unit, Q and dO rows resident as MFMA operands, K/V
 //     blocks of 64 keys through a two-slot LDS ring; per block S^T = K Q^T and dP^T = V dO^T (one lane
@@ -37,11 +37,6 @@
 namespace fa {
 
 namespace {
-
-constexpr int kBwdWaves = 4;
-constexpr int kBwdBC = 32 * kBwdWaves;  // keys per bwd_kv workgroup (32 per wave)
-constexpr int kBwdBR = 64;              // query rows per bwd_kv tile
-constexpr int kBwdSlots = 3;            // ring depth
 
 // 16-byte slot swizzle of row r of a staged tile with `rowb`-byte rows: 16 consecutive
 // rows read at one logical slot hit 16 different slots, and 8 consecutive rows read over
@@ -61,24 +56,6 @@ constexpr bool swz_period_ok() {
   return true;
 }
 
-template <int D>
-struct BwdTile {
-  static constexpr int KS = D / 16;                       // k-steps over the head dim
-  static constexpr int DB = D / 32;                       // 32-column blocks of the head dim
-  static constexpr int ROWB = D * 2;                      // bytes per staged row
-  static constexpr int SPR = D / 8;                       // 16-byte slots per row
-  static constexpr int RPI = 1024 / ROWB;                 // rows per wave DMA instruction
-  static constexpr int QBYTES = kBwdBR * ROWB;            // one Q or dO tile
-  static constexpr int NDMA = QBYTES / (1024 * kBwdWaves);  // per thread per tensor
-  static constexpr int NDMA_KV = kBwdBC * ROWB / (1024 * kBwdWaves);
-  static constexpr int STATS = 2 * QBYTES;                // offset of the statistics
-  static constexpr int SLOT = 2 * QBYTES + 1024;          // Q, dO, 64 x (lse2, D_i) + pad
-  static constexpr int RING = kBwdSlots * SLOT;
-  static constexpr int KVBYTES = 2 * kBwdBC * ROWB;       // K and V tiles (set-up only)
-  static constexpr int LDS_BYTES = RING > KVBYTES ? RING : KVBYTES;
-  static_assert(NDMA * 1024 * kBwdWaves == QBYTES, "a tile must split evenly over the waves");
-  static __host__ __device__ constexpr int swz(int r) { return swz_rows<ROWB>(r); }
-};
 
 // Per query row: stats = (LSE * log2 e, D_i = sum_d dO_id O_id).  Rows whose LSE is -inf
 // (no visible key) get +inf, so their P is exactly zero.
@@ -110,22 +87,59 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------------------------
+// dK/dV: key-tile outer loop, each 32-key group's work split between two waves.
+// ------------------------------------------------------------------------------------
+// Eight waves share a 128-key tile.  Waves 0-3 form S = Q K^T, P and dV += P^T dO for
+// their 32 keys; waves 4-7 form dP = dO V^T, dS = P (dP - D_i) and dK += dS^T Q for the
+// same keys, reading P from LDS.  Each wave keeps one operand (K or V) and one
+// accumulator in registers, so two waves fit per SIMD and the two roles' MFMA and VALU
+// phases interleave on it (one wave holding both, about 450 registers, ran one wave
+// per SIMD with every LDS and MFMA latency exposed).  Per query tile: S and dP, a
+// barrier (P published), dV and dK, a barrier (ring slot and P buffer free).
+constexpr int kKvWaves = 8;
+constexpr int kKvBC = 128;  // keys per workgroup (32 per key group)
+constexpr int kKvBR = 64;   // query rows per tile
+constexpr int kKvSlots = 3;  // ring depth
+
+template <int D>
+struct KvTile {
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int ROWB = D * 2;
+  static constexpr int SPR = D / 8;
+  static constexpr int RPI = 1024 / ROWB;
+  static constexpr int QBYTES = kKvBR * ROWB;
+  static constexpr int NDMA = QBYTES / (1024 * kKvWaves);            // per thread per tensor
+  static constexpr int NDMA_KV = kKvBC * ROWB / (1024 * kKvWaves);
+  static constexpr int STATS = 2 * QBYTES;
+  static constexpr int SLOT = 2 * QBYTES + 1024;
+  static constexpr int RING = kKvSlots * SLOT;
+  static constexpr int PX = RING;                   // P of each key group: 32 fp32 per lane
+  static constexpr int PXG = 32 * 64 * 4;           // bytes per key group
+  static constexpr int KVBYTES = 2 * kKvBC * ROWB;  // K and V staging (set-up only)
+  static constexpr int LDS_BYTES = RING + 4 * PXG > KVBYTES ? RING + 4 * PXG : KVBYTES;
+  static_assert(NDMA * 1024 * kKvWaves == QBYTES, "a tile must split evenly over the waves");
+  static_assert(NDMA_KV * 1024 * kKvWaves == kKvBC * ROWB, "K/V must split evenly");
+  static __host__ __device__ constexpr int swz(int r) { return swz_rows<ROWB>(r); }
+};
+
 template <int D, bool DROP = false>
-__global__ void __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_kv_kernel(BwdParams p) {
-  using T = BwdTile<D>;
-  constexpr int BC = kBwdBC, BR = kBwdBR, NW = kBwdWaves, NS = kBwdSlots;
-  // dropout: per wave a 32 x 64 byte table of the tile's mask, [key][query]
-  constexpr int ZBYTES = DROP ? NW * 32 * BR : 0;
+  using T = KvTile<D>;
+  constexpr int BC = kKvBC, BR = kKvBR, NW = kKvWaves, NS = kKvSlots;
+  // dropout: per key group a 32 x 64 byte table of the tile's mask, [key][query]
+  constexpr int ZBYTES = DROP ? 4 * 32 * BR : 0;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[T::LDS_BYTES + ZBYTES];
   unsigned char* ring = lds;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool dv_role = wave < 4;  // else the dP / dS / dK role
+  const int kg = wave & 3;        // key group
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // tile: each XCD holds whole (batch entry, KV head) groups; inside, key tiles in rank
-  // order, so the heaviest (causal: low key tiles see the most query tiles) go first
   const TileId tix = tile_order(blockIdx.x, gridDim.x, p.B * p.Hkv, p.nkt, 1);
   const int kt = tix.rank;
   const int hkv = tix.pair % p.Hkv;
@@ -138,12 +152,11 @@ bwd_kv_kernel(BwdParams p) {
   }
   const int diag = lk - p.Nq;
   const int k0 = kt * BC;
-  const int kwl = wave * 32 + l32;  // this lane's key within the tile (column of S, P, dS)
+  const int kwl = kg * 32 + l32;  // this lane's key within the tile (column of S, P, dS)
   const int kw = k0 + kwl;
 
-  // DMA geometry shared by every staged tile: thread (wave w, lane) fills, for
-  // instruction i, row RPI (NW i + w) + lane / SPR, slot lane % SPR; the row's swizzle
-  // does not depend on i, whose row step goes into the scalar offset.
+  // DMA geometry: thread (wave w, lane) fills, for instruction i, row RPI (NW i + w) +
+  // lane / SPR, slot lane % SPR
   const int drow = T::RPI * wave + lane / T::SPR, dslot = lane % T::SPR;
   const int dswz = dslot ^ T::swz(drow);
   auto dma_rows = [&](const uint16_t* base, int64_t pitch_el, int rows, int nrows_total,
@@ -155,7 +168,8 @@ bwd_kv_kernel(BwdParams p) {
     for (int i = 0; i < ninst; ++i) lds_dma16(rs, dst + 1024 * (NW * i + wave), off, 0, step * i);
   };
 
-  // ---- set-up: K and V tiles into LDS, then the resident operands
+  // ---- set-up: K and V tiles into LDS, then each wave's resident operand: K rows (dV
+  //      role, B operand of S = Q K^T) or V rows (dK role, of dP = dO V^T)
   {
     const int valid = k0 < lk ? lk - k0 : 0;
     dma_rows(p.k + b * p.ks0 + hkv * p.ks1 + (int64_t)k0 * p.ks2, p.ks2, BC, valid, ring, T::NDMA_KV);
@@ -164,48 +178,34 @@ bwd_kv_kernel(BwdParams p) {
     FA_WAIT_VMCNT(0);
     __syncthreads();
   }
-  // K, V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T
-  u32x4_t kf[T::KS], vf[T::KS];
+  u32x4_t kv[T::KS];
   {
     const int sw = T::swz(kwl);
+    const unsigned char* src = ring + (dv_role ? 0 : BC * T::ROWB);
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) {
-      const int o = kwl * T::ROWB + 16 * ((2 * ks + hi) ^ sw);
-      kf[ks] = *reinterpret_cast<const u32x4_t*>(ring + o);
-      vf[ks] = *reinterpret_cast<const u32x4_t*>(ring + BC * T::ROWB + o);
-    }
+    for (int ks = 0; ks < T::KS; ++ks)
+      kv[ks] = *reinterpret_cast<const u32x4_t*>(src + kwl * T::ROWB + 16 * ((2 * ks + hi) ^ sw));
   }
   FA_WAIT_LGKMCNT0();
-  __syncthreads();  // the ring reuses the K/V staging area
+  __syncthreads();  // the ring reuses the staging area
 
-  // Transposing-read geometry (lane 16 g + i reads row 16 ts + 8 r + 4 (g/2) + i/4 and 4
-  // columns from 32 blk + 16 (g%2) + 4 (i%4)).
   const int vg = lane >> 4, vi = lane & 15;
   const int vrow = 4 * (vg >> 1) + (vi >> 2);
   const int vlo = 2 * (vg & 1) + ((vi & 3) >> 1);
-  auto tr_off = [&](int rowb, int r, int blk, int swz_row) {  // byte offset in a tile
-    const int row = 8 * r + vrow;
-    return row * rowb + 16 * ((4 * blk + vlo) ^ swz_row) + 8 * (vi & 1);
-  };
 
-  f32x16_t dk[T::DB], dv[T::DB];
+  f32x16_t acc[T::DB];  // dV (dV role) or dK / scale (dK role)
 #pragma unroll
-  for (int d = 0; d < T::DB; ++d) dk[d] = dv[d] = f32x16_t{};
+  for (int d = 0; d < T::DB; ++d) acc[d] = f32x16_t{};
 
   const int nqt = (p.Nq + BR - 1) / BR;
   int qt0 = 0;
   if (p.causal) {
-    const int first_q = k0 - diag;  // first query row that sees key k0
+    const int first_q = k0 - diag;
     qt0 = first_q <= 0 ? 0 : first_q / BR;
   }
   const int per_head = (k0 < lk) ? (nqt > qt0 ? nqt - qt0 : 0) : 0;
   const int iters = per_head * p.G;
-  // Tile order: last query tile first, the group's heads innermost.  Every key tile of
-  // a KV head then visits the same (query tile, head) at about the same time, so the
-  // tile's Q and dO rows are shared in L2.
 
-  // one query tile `it` into ring slot `slot`; past the last tile the descriptors are
-  // empty and the slot is filled with zeros
   auto issue = [&](int it, int slot) {
     unsigned char* dst = ring + slot * T::SLOT;
     int gi = 0, q0 = 0, rows = 0;
@@ -226,26 +226,31 @@ bwd_kv_kernel(BwdParams p) {
   };
   // the previous tile's loads must have landed: all but this wave's latest group
   auto wait_ring = [&]() {
-    if constexpr (T::NDMA == 4) {
-      if (wave == 0) FA_WAIT_VMCNT(9); else FA_WAIT_VMCNT(8);
-    } else {
+    if constexpr (T::NDMA == 2) {
       if (wave == 0) FA_WAIT_VMCNT(5); else FA_WAIT_VMCNT(4);
+    } else {
+      if (wave == 0) FA_WAIT_VMCNT(3); else FA_WAIT_VMCNT(2);
     }
   };
-  static_assert(T::NDMA == 4 || T::NDMA == 2, "ring waits assume D = 128 or 64");
+  static_assert(T::NDMA == 2 || T::NDMA == 1, "ring waits assume D = 128 or 64");
 
-  const int qsw = T::swz(l32);  // plain reads of query rows 32 qb + l32
+  const int qsw = T::swz(l32);
   const uint32_t ring_addr = lds_addr(ring);
-  // transposing reads of slot 0: rows 8 r + vrow (+ 16 ts, an immediate: the row's
-  // swizzle does not depend on ts), 32-column block blk
+  // transposing reads of slot 0 (dO for the dV role, Q for the dK role): rows 8 r + vrow
+  // (+ 16 ts as an immediate), 32-column block blk
   uint32_t trb[2][T::DB];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int blk = 0; blk < T::DB; ++blk)
-      trb[r][blk] = ring_addr + tr_off(T::ROWB, r, blk, T::swz(8 * r + vrow));
+    for (int blk = 0; blk < T::DB; ++blk) {
+      const int row = 8 * r + vrow;
+      trb[r][blk] = ring_addr + (dv_role ? T::QBYTES : 0) + row * T::ROWB +
+                    16 * ((4 * blk + vlo) ^ T::swz(row)) + 8 * (vi & 1);
+    }
   static_assert(swz_period_ok<T::ROWB>(), "transposing-read swizzle must repeat every 16 rows");
   const float c = p.scale_log2;
+  unsigned char* px = lds + T::PX + kg * T::PXG + 16 * lane;  // + 1024 per 4 registers
+  unsigned char* zt = lds + T::LDS_BYTES + kg * 32 * BR;
 
   if (iters > 0) {
     issue(0, 0);
@@ -254,62 +259,99 @@ bwd_kv_kernel(BwdParams p) {
     FA_BARRIER();
   }
 
-  // One query tile; `slot_c` is it % NS as a compile-time constant, so every LDS
-  // operand address is a per-lane register plus an immediate offset.
   auto tile = [&](int it, auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
     issue(it + 2, (slot + 2) % NS);
     const int qt = nqt - 1 - it / p.G;
     const int q0 = qt * BR;
     const unsigned char* qs = ring + slot * T::SLOT;
-    const unsigned char* dos = qs + T::QBYTES;
     const float* st = reinterpret_cast<const float*>(qs + T::STATS);
 
-    // (1) S = Q K^T and dP = dO V^T; rows = queries 32 qb + (register), column = key
-    f32x16_t s[2], dp[2];
+    // (1) S = Q K^T (dV role) or dP = dO V^T (dK role); rows = queries 32 qb + (register),
+    //     column = key
+    const unsigned char* arows = qs + (dv_role ? 0 : T::QBYTES);
+    f32x16_t sp[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = dp[qb] = f32x16_t{};
+      sp[qb] = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
         const int o = (32 * qb + l32) * T::ROWB + 16 * ((2 * ks + hi) ^ qsw);
-        const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(qs + o);
-        const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(dos + o);
-        s[qb] = mfma32(aq, kf[ks], s[qb]);
-        dp[qb] = mfma32(ad, vf[ks], dp[qb]);
+        sp[qb] = mfma32(*reinterpret_cast<const u32x4_t*>(arows + o), kv[ks], sp[qb]);
       }
     }
 
-    // dropout mask of this wave's 32 keys and the tile's 64 queries: lane L draws the
-    // two 16-key groups of query q0 + L (the forward's words), spreads the 32 bytes into
-    // the wave's [key][query] table, and reads back the 4-query words of its own key
-    uint32_t zq[2][4] = {};
-    if constexpr (DROP) {
-      const int hq = hkv * p.G + (it % p.G);
-      unsigned char* zt = lds + T::LDS_BYTES + wave * 32 * BR;
-      const int chunk = (k0 + 32 * wave) / 32;
+    u32x4_t pk[2][2];  // P^T (dV role) or dS^T (dK role) as A operands
+    if (dv_role) {
+      // dropout mask of the group's 32 keys and the tile's 64 queries (as the forward
+      // draws it), spread into the group's [key][query] table for both roles
+      uint32_t zq[2][4] = {};
+      if constexpr (DROP) {
+        const int hq = hkv * p.G + (it % p.G);
+        const int chunk = (k0 + 32 * kg) / 32;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const u32x4_t w = dropout_words(chunk, h2, q0 + lane, hq, b, p.seed_lo, p.seed_hi);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const u32x4_t w = dropout_words(chunk, h2, q0 + lane, hq, b, p.seed_lo, p.seed_hi);
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+          for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            zt[(4 * h2 + 8 * a + e) * BR + lane] = (unsigned char)((w[a] >> (8 * e)) & 0xffu);
+            for (int e = 0; e < 4; ++e)
+              zt[(4 * h2 + 8 * a + e) * BR + lane] = (unsigned char)((w[a] >> (8 * e)) & 0xffu);
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg)
+            zq[qb][rg] = *reinterpret_cast<const uint32_t*>(zt + l32 * BR + 32 * qb + 8 * rg + 4 * hi);
       }
+      // P = exp(S - LSE), zero where the pair does not exist (two instances: tiles that
+      // cross no edge test nothing); the plain P goes to the dK role through LDS, the
+      // kept P / keep is the A operand of dV += P^T dO
+      const bool edge = (k0 + BC > lk) || (q0 + BR > p.Nq) || (p.causal && k0 + BC - 1 > q0 + diag);
+      auto probs = [&](auto masked) {
+        constexpr bool M = decltype(masked)::value;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int ql = 32 * qb + 8 * rg + 4 * hi;
+            const f32x4_t st01 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql);
+            const f32x4_t st23 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql + 4);
+            const float l2[4] = {st01[0], st01[2], st23[0], st23[2]};
+            f32x4_t pv4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float pv = fast_exp2(fmaf(sp[qb][4 * rg + e], c, -l2[e]));
+              if constexpr (M) {
+                const int q = q0 + ql + e;
+                const int lastk = min(lk - 1, p.causal ? q + diag : lk - 1);
+                pv = ((q < p.Nq) & (kw <= lastk)) ? pv : 0.f;
+              }
+              pv4[e] = pv;
+              if constexpr (DROP)
+                sp[qb][4 * rg + e] = dropout_keep(zq[qb][rg], e, p.drop_t) ? pv * p.drop_scale : 0.f;
+              else
+                sp[qb][4 * rg + e] = pv;
+            }
+            *reinterpret_cast<f32x4_t*>(px + 1024 * (4 * qb + rg)) = pv4;
+          }
+      };
+      if (edge)
+        probs(std::true_type{});
+      else
+        probs(std::false_type{});
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg)
-          zq[qb][rg] = *reinterpret_cast<const uint32_t*>(zt + l32 * BR + 32 * qb + 8 * rg + 4 * hi);
-    }
-
-    // (2) P = exp(S - LSE), dS = P (dP - D_i); zero where the pair does not exist.  Two
-    //     instances: tiles that cross no edge run without any per-element test.  With
-    //     dropout, dV takes the kept P / keep and dP is masked and scaled the same way.
-    const bool edge = (k0 + BC > lk) || (q0 + BR > p.Nq) || (p.causal && k0 + BC - 1 > q0 + diag);
-    auto probs = [&](auto masked) {
-      constexpr bool M = decltype(masked)::value;
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            pk[qb][h2][w] = pack_bf16(sp[qb][8 * h2 + 2 * w], sp[qb][8 * h2 + 2 * w + 1]);
+      FA_WAIT_LGKMCNT0();  // P (and the mask table) written
+      FA_BARRIER();
+    } else {
+      FA_BARRIER();        // P of this tile published
+      // dS = P (dP - D_i) (with dropout: dP masked and scaled as the forward's P was)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -317,83 +359,60 @@ bwd_kv_kernel(BwdParams p) {
           const int ql = 32 * qb + 8 * rg + 4 * hi;
           const f32x4_t st01 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql);
           const f32x4_t st23 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql + 4);
-          const float l2[4] = {st01[0], st01[2], st23[0], st23[2]};
           const float dd[4] = {st01[1], st01[3], st23[1], st23[3]};
+          const f32x4_t pv4 = *reinterpret_cast<const f32x4_t*>(px + 1024 * (4 * qb + rg));
+          uint32_t zw = 0;
+          if constexpr (DROP)
+            zw = *reinterpret_cast<const uint32_t*>(zt + l32 * BR + 32 * qb + 8 * rg + 4 * hi);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float pv = fast_exp2(fmaf(s[qb][4 * rg + e], c, -l2[e]));
-            if constexpr (M) {
-              const int q = q0 + ql + e;
-              const int lastk = min(lk - 1, p.causal ? q + diag : lk - 1);  // last key q sees
-              pv = ((q < p.Nq) & (kw <= lastk)) ? pv : 0.f;
-            }
-            if constexpr (DROP) {
-              const float zs = dropout_keep(zq[qb][rg], e, p.drop_t) ? p.drop_scale : 0.f;
-              s[qb][4 * rg + e] = pv * zs;
-              dp[qb][4 * rg + e] = pv * (dp[qb][4 * rg + e] * zs - dd[e]);
-            } else {
-              s[qb][4 * rg + e] = pv;
-              dp[qb][4 * rg + e] = pv * (dp[qb][4 * rg + e] - dd[e]);
-            }
+            float dpz = sp[qb][4 * rg + e];
+            if constexpr (DROP) dpz = dropout_keep(zw, e, p.drop_t) ? dpz * p.drop_scale : 0.f;
+            sp[qb][4 * rg + e] = pv4[e] * (dpz - dd[e]);
           }
         }
-    };
-    if (edge)
-      probs(std::true_type{});
-    else
-      probs(std::false_type{});
-    // P^T and dS^T as A operands: rows = keys, k-elements = queries in register order
-    u32x4_t pa[2][2], da[2][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pa[qb][h2][w] = pack_bf16(s[qb][8 * h2 + 2 * w], s[qb][8 * h2 + 2 * w + 1]);
-          da[qb][h2][w] = pack_bf16(dp[qb][8 * h2 + 2 * w], dp[qb][8 * h2 + 2 * w + 1]);
-        }
+          for (int w = 0; w < 4; ++w)
+            pk[qb][h2][w] = pack_bf16(sp[qb][8 * h2 + 2 * w], sp[qb][8 * h2 + 2 * w + 1]);
+    }
 
-    // (3) dV += P^T dO and dK += dS^T Q; k-step ts = 2 qb + h2 holds queries
-    //     16 ts + 8 (e/4) + 4 hi + e%4, which the transposing reads of dO and Q reproduce
+    // (2) acc += pk x (dO rows for the dV role, Q rows for the dK role), k-step ts = 2 qb
+    //     + h2 holding queries 16 ts + 8 (e/4) + 4 hi + e%4, which the transposing reads
+    //     reproduce
 #pragma unroll
     for (int d0 = 0; d0 < T::DB; d0 += 2) {
-      u32x2_t o[2][4][2], q[2][4][2];
-      // the slot offset goes into the instruction's 16-bit immediate where it fits
-      constexpr int TS = 16 * T::ROWB;  // k-step ts: 16 query rows further
-      constexpr bool kImm = slot * T::SLOT + 3 * TS + T::QBYTES < 65536;
+      u32x2_t f[2][4][2];
+      constexpr int TS = 16 * T::ROWB;
+      constexpr bool kImm = slot * T::SLOT + 3 * TS < 65536;
       constexpr int SO = kImm ? slot * T::SLOT : 0;
 #pragma unroll
       for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const uint32_t a = trb[r][d0 + dd] + (kImm ? 0u : (uint32_t)(slot * T::SLOT));
-          lds_read_tr16x2<SO, SO + T::QBYTES>(q[dd][0][r], o[dd][0][r], a);
-          lds_read_tr16x2<SO + TS, SO + TS + T::QBYTES>(q[dd][1][r], o[dd][1][r], a);
-          lds_read_tr16x2<SO + 2 * TS, SO + 2 * TS + T::QBYTES>(q[dd][2][r], o[dd][2][r], a);
-          lds_read_tr16x2<SO + 3 * TS, SO + 3 * TS + T::QBYTES>(q[dd][3][r], o[dd][3][r], a);
+          lds_read_tr16x2<SO, SO + TS>(f[dd][0][r], f[dd][1][r], a);
+          lds_read_tr16x2<SO + 2 * TS, SO + 3 * TS>(f[dd][2][r], f[dd][3][r], a);
         }
 #pragma unroll
       for (int dd = 0; dd < 2; ++dd) {
-        lds_wait_tr(o[dd][0][0], o[dd][0][1], o[dd][1][0], o[dd][1][1]);
-        lds_wait_tr(o[dd][2][0], o[dd][2][1], o[dd][3][0], o[dd][3][1]);
-        lds_wait_tr(q[dd][0][0], q[dd][0][1], q[dd][1][0], q[dd][1][1]);
-        lds_wait_tr(q[dd][2][0], q[dd][2][1], q[dd][3][0], q[dd][3][1]);
+        lds_wait_tr(f[dd][0][0], f[dd][0][1], f[dd][1][0], f[dd][1][1]);
+        lds_wait_tr(f[dd][2][0], f[dd][2][1], f[dd][3][0], f[dd][3][1]);
       }
 #pragma unroll
       for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
-        for (int ts = 0; ts < 4; ++ts) {
-          const int d = d0 + dd;
-          dv[d] = mfma32(pa[ts >> 1][ts & 1],
-                         u32x4_t{o[dd][ts][0][0], o[dd][ts][0][1], o[dd][ts][1][0], o[dd][ts][1][1]}, dv[d]);
-          dk[d] = mfma32(da[ts >> 1][ts & 1],
-                         u32x4_t{q[dd][ts][0][0], q[dd][ts][0][1], q[dd][ts][1][0], q[dd][ts][1][1]}, dk[d]);
-        }
+        for (int ts = 0; ts < 4; ++ts)
+          acc[d0 + dd] = mfma32(pk[ts >> 1][ts & 1],
+                                u32x4_t{f[dd][ts][0][0], f[dd][ts][0][1], f[dd][ts][1][0], f[dd][ts][1][1]},
+                                acc[d0 + dd]);
     }
 
     wait_ring();         // tile it + 1 has landed (only tile it + 2 may be in flight)
-    FA_WAIT_LGKMCNT0();  // this wave's ring reads are done
+    FA_WAIT_LGKMCNT0();  // this wave's ring and P reads are done
     FA_BARRIER();
   };
   static_assert(NS == 3, "the loop below walks three slots");
@@ -406,27 +425,21 @@ bwd_kv_kernel(BwdParams p) {
   if (it < iters) tile(it, std::integral_constant<int, 0>{});
   if (it + 1 < iters) tile(it + 1, std::integral_constant<int, 1>{});
 
-  // ---- dK = scale * acc, dV = acc, rounded to bf16; rows >= Nk are not stored (rows in
-  //      [Lk, Nk) hold zeros).  Column d = 32 blk + l32, register r holds key
-  //      8 (r/4) + 4 hi + r%4 of this wave's 32 keys.
-  uint16_t* dkb = p.dk + b * p.dks0 + hkv * p.dks1;
-  uint16_t* dvb = p.dv + b * p.dvs0 + hkv * p.dvs1;
+  // ---- dV = acc (dV role) or dK = scale * acc (dK role), rounded to bf16; rows >= Nk
+  //      are not stored.  Column d = 32 blk + l32, register r holds key 8 (r/4) + 4 hi +
+  //      r%4 of the group's 32 keys.
+  uint16_t* gb = dv_role ? p.dv + b * p.dvs0 + hkv * p.dvs1 : p.dk + b * p.dks0 + hkv * p.dks1;
+  const int64_t gs = dv_role ? p.dvs2 : p.dks2;
+  const float sc = dv_role ? 1.f : p.scale;
 #pragma unroll
   for (int d = 0; d < T::DB; ++d)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const int key0 = k0 + wave * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      const int key0 = k0 + kg * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
       const int col = 32 * d + l32;
-      const uint32_t kk = pack_bf16(dk[d][r] * p.scale, dk[d][r + 1] * p.scale);
-      const uint32_t vv = pack_bf16(dv[d][r], dv[d][r + 1]);
-      if (key0 < p.Nk) {
-        dkb[(int64_t)key0 * p.dks2 + col] = static_cast<uint16_t>(kk & 0xffffu);
-        dvb[(int64_t)key0 * p.dvs2 + col] = static_cast<uint16_t>(vv & 0xffffu);
-      }
-      if (key0 + 1 < p.Nk) {
-        dkb[(int64_t)(key0 + 1) * p.dks2 + col] = static_cast<uint16_t>(kk >> 16);
-        dvb[(int64_t)(key0 + 1) * p.dvs2 + col] = static_cast<uint16_t>(vv >> 16);
-      }
+      const uint32_t g2 = pack_bf16(acc[d][r] * sc, acc[d][r + 1] * sc);
+      if (key0 < p.Nk) gb[(int64_t)key0 * gs + col] = static_cast<uint16_t>(g2 & 0xffffu);
+      if (key0 + 1 < p.Nk) gb[(int64_t)(key0 + 1) * gs + col] = static_cast<uint16_t>(g2 >> 16);
     }
 }
 
@@ -702,8 +715,8 @@ hipError_t launch_all(BwdParams p, hipStream_t stream) {
   constexpr int RPB = 256 / (D / 8);
   hipError_t e = launch(bwd_pre_kernel<D>, (rows + RPB - 1) / RPB, 256, p, stream);
   if (e != hipSuccess) return e;
-  p.nkt = (p.Nk + kBwdBC - 1) / kBwdBC;
-  e = launch(bwd_kv_kernel<D, DROP>, (int64_t)p.nkt * p.Hkv * p.B, 64 * kBwdWaves, p, stream);
+  p.nkt = (p.Nk + kKvBC - 1) / kKvBC;
+  e = launch(bwd_kv_kernel<D, DROP>, (int64_t)p.nkt * p.Hkv * p.B, 64 * kKvWaves, p, stream);
   if (e != hipSuccess) return e;
   // 128-row query tiles, two workgroups per compute unit: finer causal load balance than
   // 256-row tiles at these grid sizes (measured 0.91 -> 0.80 ms for B2 H16 N4096 D128)
