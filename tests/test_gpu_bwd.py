@@ -88,6 +88,27 @@ def test_bwd_is_deterministic():
         assert torch.equal(x1, x2)
 
 
+def test_bwd_strided_layout_bnhd_gives_the_same_bits():
+    # [B, N, H, D] memory (the flash-attn layout) for every input and gradient, passed
+    # through strides: the kernels do the same arithmetic, so the results are identical
+    say("bwd strided layout")
+    x = inputs.attention_inputs(2, 4, 2, 200, 200, 128, "bf16", seed=9, with_grad=True)
+    q, k, v, do = to_dev(x.q), to_dev(x.k), to_dev(x.v), to_dev(x.do)
+    o, lse = fa.fwd(q, k, v, causal=True)
+    ref = fa.bwd(q, k, v, o, do, lse, causal=True)
+
+    def bnhd(t):
+        return t.transpose(1, 2).contiguous().transpose(1, 2)
+
+    qn, kn, vn, on, don = (bnhd(t) for t in (q, k, v, o, do))
+    grads = (bnhd(torch.empty_like(q)), bnhd(torch.empty_like(k)), bnhd(torch.empty_like(v)))
+    got = fa.bwd(qn, kn, vn, on, don, lse, causal=True, grads=grads)
+    torch.cuda.synchronize()
+    assert not grads[0].is_contiguous()
+    for g, r in zip(got, ref):
+        assert torch.equal(g, r)
+
+
 def test_bwd_gqa_full_size_c3_shape():
     # B1 Hq32 Hkv8 N16384 D128 causal: sampled dQ rows against the oracle; dK and dV
     # against the MHA backward with every KV head repeated for its 4 query heads,

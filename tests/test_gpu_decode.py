@@ -88,3 +88,21 @@ def test_decode_full_size_c5_sampled_sequences():
     seqs = [int(np.argmin(d.seq_lens)), int(np.argmax(d.seq_lens)), 0, 17, 63]
     o_ref, lse_ref = oracle_decode(d, seqs)
     assert_fwd_close(to_host(o[seqs]), to_host(lse[seqs]), o_ref, lse_ref, True)
+
+
+def test_decode_strided_cache_layout_gives_the_same_bits():
+    # a [Bs, Lmax, Hkv, D] cache (heads interleaved per position) passed through strides
+    rng = np.random.default_rng(7)
+    lens = [2500, 700, 4100]
+    d = inputs.DecodeInputs(np.array(lens), inputs.bf16_round(rng.standard_normal((3, 8, 128), dtype=np.float32)),
+                            2, 128, seed=3)
+    kc, vc = build_cache(d, 4200)
+    q = torch.from_numpy(d.q).to(DEV).to(torch.bfloat16)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    a = fa.decode(q, kc, vc, sl, max_len=4200, split_len=1024)
+    kn = kc.transpose(1, 2).contiguous().transpose(1, 2)
+    vn = vc.transpose(1, 2).contiguous().transpose(1, 2)
+    b = fa.decode(q, kn, vn, sl, max_len=4200, split_len=1024)
+    torch.cuda.synchronize()
+    assert kn.stride(2) == 2 * 128 and torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
