@@ -282,28 +282,24 @@ bwd_kv_kernel(BwdParams p) {
     }
 
     u32x4_t pk[2][2];  // P^T (dV role) or dS^T (dK role) as A operands
+    // dropout: the mask of the group's 32 keys and the tile's 64 queries, drawn as the
+    // forward draws it (lane L: the words of query q0 + L) and spread into the group's
+    // [key][query] byte table; each role draws one of the two 16-key halves
+    auto draw_mask_half = [&](int h2) {
+      const int hq = hkv * p.G + (it % p.G);
+      const u32x4_t w = dropout_words((k0 + 32 * kg) / 32, h2, q0 + lane, hq, b, p.seed_lo, p.seed_hi);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          zt[(4 * h2 + 8 * a + e) * BR + lane] = (unsigned char)((w[a] >> (8 * e)) & 0xffu);
+    };
+    // the table's 4-query word of this lane's key for query rows 32 qb + 8 rg + 4 hi ..
+    auto mask_word = [&](int qb, int rg) {
+      return *reinterpret_cast<const uint32_t*>(zt + l32 * BR + 32 * qb + 8 * rg + 4 * hi);
+    };
     if (dv_role) {
-      // dropout mask of the group's 32 keys and the tile's 64 queries (as the forward
-      // draws it), spread into the group's [key][query] table for both roles
-      uint32_t zq[2][4] = {};
-      if constexpr (DROP) {
-        const int hq = hkv * p.G + (it % p.G);
-        const int chunk = (k0 + 32 * kg) / 32;
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const u32x4_t w = dropout_words(chunk, h2, q0 + lane, hq, b, p.seed_lo, p.seed_hi);
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              zt[(4 * h2 + 8 * a + e) * BR + lane] = (unsigned char)((w[a] >> (8 * e)) & 0xffu);
-        }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int rg = 0; rg < 4; ++rg)
-            zq[qb][rg] = *reinterpret_cast<const uint32_t*>(zt + l32 * BR + 32 * qb + 8 * rg + 4 * hi);
-      }
+      if constexpr (DROP) draw_mask_half(0);
       // P = exp(S - LSE), zero where the pair does not exist (two instances: tiles that
       // cross no edge test nothing); the plain P goes to the dK role through LDS, the
       // kept P / keep is the A operand of dV += P^T dO
@@ -328,10 +324,7 @@ bwd_kv_kernel(BwdParams p) {
                 pv = ((q < p.Nq) & (kw <= lastk)) ? pv : 0.f;
               }
               pv4[e] = pv;
-              if constexpr (DROP)
-                sp[qb][4 * rg + e] = dropout_keep(zq[qb][rg], e, p.drop_t) ? pv * p.drop_scale : 0.f;
-              else
-                sp[qb][4 * rg + e] = pv;
+              sp[qb][4 * rg + e] = pv;
             }
             *reinterpret_cast<f32x4_t*>(px + 1024 * (4 * qb + rg)) = pv4;
           }
@@ -340,6 +333,19 @@ bwd_kv_kernel(BwdParams p) {
         probs(std::true_type{});
       else
         probs(std::false_type{});
+      FA_WAIT_LGKMCNT0();  // P and this role's half of the mask table written
+      FA_BARRIER();
+      if constexpr (DROP) {  // dV takes the kept P / keep
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const uint32_t zw = mask_word(qb, rg);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sp[qb][4 * rg + e] = dropout_keep(zw, e, p.drop_t) ? sp[qb][4 * rg + e] * p.drop_scale : 0.f;
+          }
+      }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -347,10 +353,12 @@ bwd_kv_kernel(BwdParams p) {
 #pragma unroll
           for (int w = 0; w < 4; ++w)
             pk[qb][h2][w] = pack_bf16(sp[qb][8 * h2 + 2 * w], sp[qb][8 * h2 + 2 * w + 1]);
-      FA_WAIT_LGKMCNT0();  // P (and the mask table) written
-      FA_BARRIER();
     } else {
-      FA_BARRIER();        // P of this tile published
+      if constexpr (DROP) {
+        draw_mask_half(1);
+        FA_WAIT_LGKMCNT0();  // this role's half of the mask table written
+      }
+      FA_BARRIER();        // P of this tile (and the whole mask table) published
       // dS = P (dP - D_i) (with dropout: dP masked and scaled as the forward's P was)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
@@ -362,8 +370,7 @@ bwd_kv_kernel(BwdParams p) {
           const float dd[4] = {st01[1], st01[3], st23[1], st23[3]};
           const f32x4_t pv4 = *reinterpret_cast<const f32x4_t*>(px + 1024 * (4 * qb + rg));
           uint32_t zw = 0;
-          if constexpr (DROP)
-            zw = *reinterpret_cast<const uint32_t*>(zt + l32 * BR + 32 * qb + 8 * rg + 4 * hi);
+          if constexpr (DROP) zw = mask_word(qb, rg);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float dpz = sp[qb][4 * rg + e];
