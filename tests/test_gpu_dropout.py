@@ -25,7 +25,7 @@ def test_dropout_mask_is_the_generators_bit_for_bit():
     x = inputs.attention_inputs(B, H, H, Nq, Nk, D, "bf16", seed=31)
     v = np.zeros((B, H, Nk, D), np.float32)
     v[:, :, np.arange(Nk), np.arange(Nk)] = 1.0
-    for p in (0.1, 0.5):
+    for p in (0.1, 0.5, 0.95):
         for causal in (False, True):
             o, _ = fa.fwd_dropout(to_dev(x.q), to_dev(x.k), to_dev(v), p, SEED, causal=causal,
                                   out_dtype=torch.float32)
@@ -48,7 +48,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-@pytest.mark.parametrize("p_drop", [0.1, 0.5])
+@pytest.mark.parametrize("p_drop", [0.1, 0.5, 0.95])
 def test_dropout_forward_and_backward_match_oracle(case, p_drop):
     name, B, Hq, Hkv, Nq, Nk, D, causal, kv_lens = case
     say(f"dropout {name} p={p_drop}")
