@@ -95,8 +95,10 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
 // same keys, reading P from LDS.  Each wave keeps one operand (K or V) and one
 // accumulator in registers, so two waves fit per SIMD and the two roles' MFMA and VALU
 // phases interleave on it (one wave holding both, about 450 registers, ran one wave
-// per SIMD with every LDS and MFMA latency exposed).  Per query tile: S and dP, a
-// barrier (P published), dV and dK, a barrier (ring slot and P buffer free).
+// per SIMD with every LDS and MFMA latency exposed).  Per query tile: S and dP, P handed
+// from one wave of the pair to the other (a flag in LDS; with dropout a workgroup
+// barrier, which also publishes the mask table), dV and dK, a barrier (ring slot and P
+// buffer free).
 constexpr int kKvWaves = 8;
 constexpr int kKvBC = 128;  // keys per workgroup (32 per key group)
 constexpr int kKvBR = 64;   // query rows per tile
@@ -118,7 +120,8 @@ struct KvTile {
   static constexpr int PX = RING;                   // P of each key group: 32 fp32 per lane
   static constexpr int PXG = 32 * 64 * 4;           // bytes per key group
   static constexpr int KVBYTES = 2 * kKvBC * ROWB;  // K and V staging (set-up only)
-  static constexpr int LDS_BYTES = RING + 4 * PXG > KVBYTES ? RING + 4 * PXG : KVBYTES;
+  static constexpr int FLAGS = PX + 4 * PXG;        // per key group: the last tile whose P is out
+  static constexpr int LDS_BYTES = FLAGS + 64 > KVBYTES ? FLAGS + 64 : KVBYTES;
   static_assert(NDMA * 1024 * kKvWaves == QBYTES, "a tile must split evenly over the waves");
   static_assert(NDMA_KV * 1024 * kKvWaves == kKvBC * ROWB, "K/V must split evenly");
   static __host__ __device__ constexpr int swz(int r) { return swz_rows<ROWB>(r); }
@@ -251,11 +254,21 @@ bwd_kv_kernel(BwdParams p) {
   const float c = p.scale_log2;
   unsigned char* px = lds + T::PX + kg * T::PXG + 16 * lane;  // + 1024 per 4 registers
   unsigned char* zt = lds + T::LDS_BYTES + kg * 32 * BR;
+  // Without dropout the two waves of a key group hand P over pairwise instead of through
+  // a workgroup barrier: the P wave stores the tile number (from 1) once its P writes have
+  // completed, and the partner polls for it.  The poll is bounded; every P wave reaches
+  // the store of every tile before its next barrier, so the bound is never the exit.
+  typedef volatile __attribute__((address_space(3))) uint32_t lds_u32;  // ds_read / ds_write
+  lds_u32* flags = (lds_u32*)(lds + T::FLAGS);
+  lds_u32* pflag = flags + kg;
+  constexpr int kMaxSpin = 1 << 16;
+  if (tid < 4) flags[tid] = 0u;
 
   if (iters > 0) {
     issue(0, 0);
     issue(1, 1);
     wait_ring();
+    FA_WAIT_LGKMCNT0();  // the flags are cleared
     FA_BARRIER();
   }
 
@@ -334,7 +347,11 @@ bwd_kv_kernel(BwdParams p) {
       else
         probs(std::false_type{});
       FA_WAIT_LGKMCNT0();  // P and this role's half of the mask table written
-      FA_BARRIER();
+      if constexpr (DROP) {
+        FA_BARRIER();
+      } else {
+        if (lane == 0) *pflag = (uint32_t)(it + 1);
+      }
       if constexpr (DROP) {  // dV takes the kept P / keep
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
@@ -357,8 +374,12 @@ bwd_kv_kernel(BwdParams p) {
       if constexpr (DROP) {
         draw_mask_half(1);
         FA_WAIT_LGKMCNT0();  // this role's half of the mask table written
+        FA_BARRIER();        // P of this tile and the whole mask table published
+      } else {
+        for (int spin = 0; *pflag != (uint32_t)(it + 1) && spin < kMaxSpin; ++spin)
+          __builtin_amdgcn_s_sleep(1);
+        asm volatile("" ::: "memory");  // the P reads below stay after the poll
       }
-      FA_BARRIER();        // P of this tile (and the whole mask table) published
       // dS = P (dP - D_i) (with dropout: dP masked and scaled as the forward's P was)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
