@@ -339,20 +339,16 @@ bwd_kv_kernel(BwdParams p) {
               pv4[e] = pv;
               sp[qb][4 * rg + e] = pv;
             }
-            *reinterpret_cast<f32x4_t*>(px + 1024 * (4 * qb + rg)) = pv4;
+            if constexpr (DROP) *reinterpret_cast<f32x4_t*>(px + 1024 * (4 * qb + rg)) = pv4;
           }
       };
       if (edge)
         probs(std::true_type{});
       else
         probs(std::false_type{});
-      FA_WAIT_LGKMCNT0();  // P and this role's half of the mask table written
-      if constexpr (DROP) {
-        FA_BARRIER();
-      } else {
-        if (lane == 0) *pflag = (uint32_t)(it + 1);
-      }
       if constexpr (DROP) {  // dV takes the kept P / keep
+        FA_WAIT_LGKMCNT0();  // P and this role's half of the mask table written
+        FA_BARRIER();
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -370,6 +366,14 @@ bwd_kv_kernel(BwdParams p) {
 #pragma unroll
           for (int w = 0; w < 4; ++w)
             pk[qb][h2][w] = pack_bf16(sp[qb][8 * h2 + 2 * w], sp[qb][8 * h2 + 2 * w + 1]);
+      if constexpr (!DROP) {  // without dropout the hand-off carries P as the bf16 dV uses
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) *reinterpret_cast<u32x4_t*>(px + 1024 * (2 * qb + h2)) = pk[qb][h2];
+        FA_WAIT_LGKMCNT0();  // P written
+        if (lane == 0) *pflag = (uint32_t)(it + 1);
+      }
     } else {
       if constexpr (DROP) {
         draw_mask_half(1);
@@ -389,7 +393,13 @@ bwd_kv_kernel(BwdParams p) {
           const f32x4_t st01 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql);
           const f32x4_t st23 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql + 4);
           const float dd[4] = {st01[1], st01[3], st23[1], st23[3]};
-          const f32x4_t pv4 = *reinterpret_cast<const f32x4_t*>(px + 1024 * (4 * qb + rg));
+          f32x4_t pv4;
+          if constexpr (DROP) {
+            pv4 = *reinterpret_cast<const f32x4_t*>(px + 1024 * (4 * qb + rg));
+          } else {  // registers 4 rg .. 4 rg + 3: words 2 (rg % 2), +1 of pair (qb, rg / 2)
+            const u32x2_t w2 = *reinterpret_cast<const u32x2_t*>(px + 1024 * (2 * qb + (rg >> 1)) + 8 * (rg & 1));
+            pv4 = f32x4_t{bf16_lo(w2[0]), bf16_hi(w2[0]), bf16_lo(w2[1]), bf16_hi(w2[1])};
+          }
           uint32_t zw = 0;
           if constexpr (DROP) zw = mask_word(qb, rg);
 #pragma unroll
