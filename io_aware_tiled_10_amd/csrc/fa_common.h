@@ -218,6 +218,13 @@ __device__ __forceinline__ void lds_wait_tr2(u32x2_t& a, u32x2_t& b) {
 __device__ __forceinline__ void lds_wait_tr(u32x2_t& a, u32x2_t& b, u32x2_t& c, u32x2_t& d) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d)::"memory");
 }
+// The same with at most N LDS operations of this wave still outstanding (LDS results
+// return in issue order, so the reads issued more than N operations ago have landed).
+template <int N>
+__device__ __forceinline__ void lds_wait_tr(u32x2_t& a, u32x2_t& b, u32x2_t& c, u32x2_t& d) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt holds 0..15");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N) : "memory");
+}
 // LDS byte address of a pointer into __shared__ memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;

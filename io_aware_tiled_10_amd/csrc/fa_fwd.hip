@@ -368,19 +368,32 @@ fwd_bf16_kernel(FwdParams p) {
     l += rs;
 
     // O^T += V^T P^T; k-step ts holds keys 16 ts + 8 (e/4) + 4 hi + e%4 (e = 0..7)
+    // the V^T reads of each 32-column block are issued before the products of the
+    // previous block, so their latency hides under those products (LDS returns in
+    // order: after issuing block d + 1, a count of 8 means block d has arrived)
+    u32x2_t v[2][4][2];
+    auto vread = [&](int d, u32x2_t (&w)[4][2]) {
+      const uint32_t a = vaddr[d];
+      lds_read_tr16x2<vo, vo + 8 * T::ROWB>(w[0][0], w[0][1], a);
+      lds_read_tr16x2<vo + 16 * T::ROWB, vo + 24 * T::ROWB>(w[1][0], w[1][1], a);
+      lds_read_tr16x2<vo + 32 * T::ROWB, vo + 40 * T::ROWB>(w[2][0], w[2][1], a);
+      lds_read_tr16x2<vo + 48 * T::ROWB, vo + 56 * T::ROWB>(w[3][0], w[3][1], a);
+    };
+    vread(0, v[0]);
 #pragma unroll
     for (int d = 0; d < T::DB; ++d) {
-      const uint32_t a = vaddr[d];
-      u32x2_t v[4][2];
-      lds_read_tr16x2<vo, vo + 8 * T::ROWB>(v[0][0], v[0][1], a);
-      lds_read_tr16x2<vo + 16 * T::ROWB, vo + 24 * T::ROWB>(v[1][0], v[1][1], a);
-      lds_read_tr16x2<vo + 32 * T::ROWB, vo + 40 * T::ROWB>(v[2][0], v[2][1], a);
-      lds_read_tr16x2<vo + 48 * T::ROWB, vo + 56 * T::ROWB>(v[3][0], v[3][1], a);
-      lds_wait_tr(v[0][0], v[0][1], v[1][0], v[1][1]);
-      lds_wait_tr(v[2][0], v[2][1], v[3][0], v[3][1]);
+      u32x2_t (&w)[4][2] = v[d & 1];
+      if (d + 1 < T::DB) {
+        vread(d + 1, v[(d + 1) & 1]);
+        lds_wait_tr<8>(w[0][0], w[0][1], w[1][0], w[1][1]);
+        lds_wait_tr<8>(w[2][0], w[2][1], w[3][0], w[3][1]);
+      } else {
+        lds_wait_tr(w[0][0], w[0][1], w[1][0], w[1][1]);
+        lds_wait_tr(w[2][0], w[2][1], w[3][0], w[3][1]);
+      }
 #pragma unroll
       for (int ts = 0; ts < 4; ++ts)
-        acc[d] = mfma32(u32x4_t{v[ts][0][0], v[ts][0][1], v[ts][1][0], v[ts][1][1]}, pf[ts], acc[d]);
+        acc[d] = mfma32(u32x4_t{w[ts][0][0], w[ts][0][1], w[ts][1][0], w[ts][1][1]}, pf[ts], acc[d]);
     }
 
     // the loads of blocks j + 2 (K) and j + 1 (V), issued one block ago, have landed
