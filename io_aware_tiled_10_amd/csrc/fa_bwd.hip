@@ -15,10 +15,12 @@
 //  2. bwd_kv: one workgroup (8 waves) per 128-key tile of a KV head, walking the 64-row
 //     query tiles of every query head of the GQA group that can see the tile (causal:
 //     from the diagonal down).  Q, dO and the row statistics of each tile stream from
-//     L2/HBM straight into a three-slot LDS ring (LDS DMA, XOR-swizzled 16-byte slots),
-//     two tiles ahead.  Each 32-key group is served by two waves: one keeps the keys' K
-//     rows and forms S = Q K^T, P and dV += P^T dO; the other keeps their V rows and
-//     forms dP = dO V^T, dS = P (dP - D_i) (P read from LDS) and dK += dS^T Q.  On
+//     L2/HBM straight into a three-slot LDS ring (LDS DMA, XOR-swizzled 16-byte slots).
+//     Each 32-key group is served by two waves: one keeps the keys' K rows and forms
+//     S = Q K^T, P and dV += P^T dO; the other keeps their V rows and forms dP = dO V^T,
+//     dS = P (dP - D_i) (P read from LDS) and dK += dS^T Q, one query tile behind the
+//     first, so it never waits for P inside a step (with dropout both take the same
+//     tile and meet at a barrier).  On
 //     32x32x16 bf16 MFMA with one lane per key, P and dS are already the A operands of
 //     the second products, whose dO^T and Q^T come from transposing LDS reads;
 //  3. bwd_q: the forward's layout turned to dQ.  One workgroup (4 waves) per 128-row
@@ -95,10 +97,11 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
 // same keys, reading P from LDS.  Each wave keeps one operand (K or V) and one
 // accumulator in registers, so two waves fit per SIMD and the two roles' MFMA and VALU
 // phases interleave on it (one wave holding both, about 450 registers, ran one wave
-// per SIMD with every LDS and MFMA latency exposed).  Per query tile: S and dP, P handed
-// from one wave of the pair to the other (a flag in LDS; with dropout a workgroup
-// barrier, which also publishes the mask table), dV and dK, a barrier (ring slot and P
-// buffer free).
+// per SIMD with every LDS and MFMA latency exposed).  Without dropout, step s: the dV
+// role takes tile s (S, P into one of two LDS buffers of its key group, dV) while the dK
+// role takes tile s - 1 (dP, dS with the P the previous step's barrier published, dK);
+// one barrier per step frees the ring slot and the P buffer.  With dropout both roles
+// take tile s and a barrier in the middle publishes P and the mask table.
 constexpr int kKvWaves = 8;
 constexpr int kKvBC = 128;  // keys per workgroup (32 per key group)
 constexpr int kKvBR = 64;   // query rows per tile
@@ -117,11 +120,11 @@ struct KvTile {
   static constexpr int STATS = 2 * QBYTES;
   static constexpr int SLOT = 2 * QBYTES + 1024;
   static constexpr int RING = kKvSlots * SLOT;
-  static constexpr int PX = RING;                   // P of each key group: 32 fp32 per lane
+  // P of each key group: 32 fp32 per lane with dropout, else two 4 KiB bf16 buffers
+  static constexpr int PX = RING;
   static constexpr int PXG = 32 * 64 * 4;           // bytes per key group
   static constexpr int KVBYTES = 2 * kKvBC * ROWB;  // K and V staging (set-up only)
-  static constexpr int FLAGS = PX + 4 * PXG;        // per key group: the last tile whose P is out
-  static constexpr int LDS_BYTES = FLAGS + 64 > KVBYTES ? FLAGS + 64 : KVBYTES;
+  static constexpr int LDS_BYTES = PX + 4 * PXG > KVBYTES ? PX + 4 * PXG : KVBYTES;
   static_assert(NDMA * 1024 * kKvWaves == QBYTES, "a tile must split evenly over the waves");
   static_assert(NDMA_KV * 1024 * kKvWaves == kKvBC * ROWB, "K/V must split evenly");
   static __host__ __device__ constexpr int swz(int r) { return swz_rows<ROWB>(r); }
@@ -254,27 +257,10 @@ bwd_kv_kernel(BwdParams p) {
   const float c = p.scale_log2;
   unsigned char* px = lds + T::PX + kg * T::PXG + 16 * lane;  // + 1024 per 4 registers
   unsigned char* zt = lds + T::LDS_BYTES + kg * 32 * BR;
-  // Without dropout the two waves of a key group hand P over pairwise instead of through
-  // a workgroup barrier: the P wave stores the tile number (from 1) once its P writes have
-  // completed, and the partner polls for it.  The poll is bounded; every P wave reaches
-  // the store of every tile before its next barrier, so the bound is never the exit.
-  typedef volatile __attribute__((address_space(3))) uint32_t lds_u32;  // ds_read / ds_write
-  lds_u32* flags = (lds_u32*)(lds + T::FLAGS);
-  lds_u32* pflag = flags + kg;
-  constexpr int kMaxSpin = 1 << 16;
-  if (tid < 4) flags[tid] = 0u;
 
-  if (iters > 0) {
-    issue(0, 0);
-    issue(1, 1);
-    wait_ring();
-    FA_WAIT_LGKMCNT0();  // the flags are cleared
-    FA_BARRIER();
-  }
-
-  auto tile = [&](int it, auto slot_c) {
-    constexpr int slot = decltype(slot_c)::value;
-    issue(it + 2, (slot + 2) % NS);
+  // One query tile `it` in ring slot `slot` (uniform over the wave); `pboff` selects the
+  // P buffer of the key group's pair.
+  auto tile = [&](int it, int slot, uint32_t pboff) __attribute__((always_inline)) {
     const int qt = nqt - 1 - it / p.G;
     const int q0 = qt * BR;
     const unsigned char* qs = ring + slot * T::SLOT;
@@ -370,9 +356,8 @@ bwd_kv_kernel(BwdParams p) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) *reinterpret_cast<u32x4_t*>(px + 1024 * (2 * qb + h2)) = pk[qb][h2];
-        FA_WAIT_LGKMCNT0();  // P written
-        if (lane == 0) *pflag = (uint32_t)(it + 1);
+          for (int h2 = 0; h2 < 2; ++h2)
+            *reinterpret_cast<u32x4_t*>(px + pboff + 1024 * (2 * qb + h2)) = pk[qb][h2];
       }
     } else {
       if constexpr (DROP) {
@@ -380,9 +365,7 @@ bwd_kv_kernel(BwdParams p) {
         FA_WAIT_LGKMCNT0();  // this role's half of the mask table written
         FA_BARRIER();        // P of this tile and the whole mask table published
       } else {
-        for (int spin = 0; *pflag != (uint32_t)(it + 1) && spin < kMaxSpin; ++spin)
-          __builtin_amdgcn_s_sleep(1);
-        asm volatile("" ::: "memory");  // the P reads below stay after the poll
+        asm volatile("" ::: "memory");  // the P reads below stay after the products above
       }
       // dS = P (dP - D_i) (with dropout: dP masked and scaled as the forward's P was)
 #pragma unroll
@@ -397,7 +380,8 @@ bwd_kv_kernel(BwdParams p) {
           if constexpr (DROP) {
             pv4 = *reinterpret_cast<const f32x4_t*>(px + 1024 * (4 * qb + rg));
           } else {  // registers 4 rg .. 4 rg + 3: words 2 (rg % 2), +1 of pair (qb, rg / 2)
-            const u32x2_t w2 = *reinterpret_cast<const u32x2_t*>(px + 1024 * (2 * qb + (rg >> 1)) + 8 * (rg & 1));
+            const u32x2_t w2 =
+                *reinterpret_cast<const u32x2_t*>(px + pboff + 1024 * (2 * qb + (rg >> 1)) + 8 * (rg & 1));
             pv4 = f32x4_t{bf16_lo(w2[0]), bf16_hi(w2[0]), bf16_lo(w2[1]), bf16_hi(w2[1])};
           }
           uint32_t zw = 0;
@@ -424,14 +408,12 @@ bwd_kv_kernel(BwdParams p) {
 #pragma unroll
     for (int d0 = 0; d0 < T::DB; d0 += 2) {
       u32x2_t f[2][4][2];
-      constexpr int TS = 16 * T::ROWB;
-      constexpr bool kImm = slot * T::SLOT + 3 * TS < 65536;
-      constexpr int SO = kImm ? slot * T::SLOT : 0;
+      constexpr int TS = 16 * T::ROWB, SO = 0;
 #pragma unroll
       for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-          const uint32_t a = trb[r][d0 + dd] + (kImm ? 0u : (uint32_t)(slot * T::SLOT));
+          const uint32_t a = trb[r][d0 + dd] + (uint32_t)__builtin_amdgcn_readfirstlane(slot * T::SLOT);
           lds_read_tr16x2<SO, SO + TS>(f[dd][0][r], f[dd][1][r], a);
           lds_read_tr16x2<SO + 2 * TS, SO + 3 * TS>(f[dd][2][r], f[dd][3][r], a);
         }
@@ -449,19 +431,44 @@ bwd_kv_kernel(BwdParams p) {
                                 acc[d0 + dd]);
     }
 
-    wait_ring();         // tile it + 1 has landed (only tile it + 2 may be in flight)
-    FA_WAIT_LGKMCNT0();  // this wave's ring and P reads are done
+  };
+  // Without dropout the dK role runs one tile behind the dV role: in step s the dV role
+  // forms P of tile s and the dK role uses P of tile s - 1, which the barrier closing step
+  // s - 1 published (P alternates between two buffers per key group), so neither role
+  // waits for the other inside a step.  The ring then loads one tile ahead: slots s - 1
+  // (dK role), s (dV role) and s + 1 (loading) are in use, and iters + 1 steps run.  With
+  // dropout both roles take tile s in step s (their barrier inside the tile publishes the
+  // mask table) and the ring loads two tiles ahead.  Every wave passes the same barriers.
+  constexpr int AHEAD = DROP ? 2 : 1, LAG = DROP ? 0 : 1;
+  auto step = [&](int st, auto slot_c) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
+    issue(st + AHEAD, (slot + AHEAD) % NS);
+    const int lag = dv_role ? 0 : LAG;
+    const int it = st - lag;
+    if (it >= 0 && it < iters) tile(it, (slot + NS - lag) % NS, (uint32_t)(it & 1) * 4096u);
+    if constexpr (DROP) wait_ring();  // tile st + 1 has landed (only st + 2 may be in flight)
+    else FA_WAIT_VMCNT(0);            // tile st + 1 has landed
+    FA_WAIT_LGKMCNT0();               // this wave's ring and P accesses are done
     FA_BARRIER();
   };
   static_assert(NS == 3, "the loop below walks three slots");
-  int it = 0;
-  for (; it + 2 < iters; it += 3) {
-    tile(it, std::integral_constant<int, 0>{});
-    tile(it + 1, std::integral_constant<int, 1>{});
-    tile(it + 2, std::integral_constant<int, 2>{});
+  if (iters > 0) {
+    issue(0, 0);
+    if constexpr (DROP) issue(1, 1);
+    if constexpr (DROP) wait_ring();
+    else FA_WAIT_VMCNT(0);
+    FA_WAIT_LGKMCNT0();
+    FA_BARRIER();
+    const int nsteps = iters + LAG;
+    int st = 0;
+    for (; st + 2 < nsteps; st += 3) {
+      step(st, std::integral_constant<int, 0>{});
+      step(st + 1, std::integral_constant<int, 1>{});
+      step(st + 2, std::integral_constant<int, 2>{});
+    }
+    if (st < nsteps) step(st, std::integral_constant<int, 0>{});
+    if (st + 1 < nsteps) step(st + 1, std::integral_constant<int, 1>{});
   }
-  if (it < iters) tile(it, std::integral_constant<int, 0>{});
-  if (it + 1 < iters) tile(it + 1, std::integral_constant<int, 1>{});
 
   // ---- dV = acc (dV role) or dK = scale * acc (dK role), rounded to bf16; rows >= Nk
   //      are not stored.  Column d = 32 blk + l32, register r holds key 8 (r/4) + 4 hi +
