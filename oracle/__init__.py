@@ -6,6 +6,7 @@ leg import this package.  It shares no code with the HIP library.
 
 from .attention import (  # noqa: F401
     attn_bwd,
+    attn_bwd_dkdv_rows,
     attn_bwd_dq_rows,
     attn_decode,
     attn_decode_paged,

@@ -59,6 +59,7 @@ __all__ = [
     "attn_fwd",
     "attn_bwd",
     "attn_bwd_dq_rows",
+    "attn_bwd_dkdv_rows",
     "attn_decode",
     "attn_fwd_varlen",
     "attn_decode_paged",
@@ -243,6 +244,58 @@ def attn_bwd_dq_rows(q, k, v, do, rows: Sequence[int], scale: Optional[float] = 
             ds = p * (doh @ vh.T - di[:, None])
             dq[b, h] = scale * (ds @ kh)
     return dq
+
+
+def attn_bwd_dkdv_rows(q, k, v, do, key_rows: Sequence[int], scale: Optional[float] = None,
+                       causal: bool = False, kv_lens: Optional[Sequence[int]] = None):
+    """dK and dV of the key rows in ``key_rows`` only, by the relations of ``attn_bwd``.
+
+    Key j's gradients are sums over the query rows i that see it, over every query
+    head of its GQA group:
+
+        dV_j = sum_i P_ij dO_i,      dK_j = scale * sum_i dS_ij Q_i,
+        dS_ij = P_ij (dP_ij - D_i),  dP_ij = dO_i . V_j,  D_i = rowsum(dO_i * O_i).
+
+    P_ij and D_i depend on the whole row i (its normaliser and its O_i), so every
+    query row that sees at least one sampled key is formed in full, exactly as in
+    ``attn_bwd``; only the sampled key columns are accumulated.  Rows that see none of
+    the sampled keys contribute nothing and are skipped.  Keys at or past kv_len do
+    not exist and get zero gradients.  Returns dk, dv [B, Hkv, len(key_rows), D] in
+    float64.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    b_, hq_, nq, d = q.shape
+    _, hkv, nk, _ = k.shape
+    g = hq_ // hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kr = np.asarray(key_rows, dtype=np.int64)
+    dk = np.zeros((b_, hkv, len(kr), d))
+    dv = np.zeros((b_, hkv, len(kr), d))
+    rows_all = np.arange(nq)
+    step = max(1, _CHUNK_ELEMS // max(nk, 1))
+    for b in range(b_):
+        lk = _kv_len_of(kv_lens, b, nk)
+        sel = kr < lk                      # sampled keys that exist
+        if not sel.any():
+            continue
+        ks = kr[sel]
+        for h in range(hq_):
+            kh, vh = k[b, h // g, :lk], v[b, h // g, :lk]
+            for c0 in range(0, nq, step):
+                rr = rows_all[c0:c0 + step]
+                vis = visible_mask(rr, nq, lk, lk, causal)
+                if not vis[:, ks].any():   # no row of the chunk sees a sampled key
+                    continue
+                s = scale * (q[b, h, rr] @ kh.T)
+                p, _ = _softmax_rows(s, vis)
+                doh = do[b, h, rr]
+                di = np.sum(doh * (p @ vh), axis=-1)
+                pj = p[:, ks]
+                dsj = pj * (doh @ vh[ks].T - di[:, None])
+                dv[b, h // g, sel] += pj.T @ doh
+                dk[b, h // g, sel] += scale * (dsj.T @ q[b, h, rr])
+    return dk, dv
 
 
 def attn_decode(q, k_cache, v_cache, seq_lens: Sequence[int],

@@ -82,8 +82,12 @@ def keep_mask(b: int, h: int, rows, nk: int, seed: int, p_drop: float) -> np.nda
 
 
 def attn_fwd_dropout(q, k, v, p_drop: float, seed: int, scale: Optional[float] = None,
-                     causal: bool = False, kv_lens=None):
-    """O = (P * Z * keep_scale) V and the undropped LSE, by the plain definition."""
+                     causal: bool = False, kv_lens=None, bh0=(0, 0)):
+    """O = (P * Z * keep_scale) V and the undropped LSE, by the plain definition.
+
+    ``bh0`` = (b0, h0) places the given tensors inside a larger batch: element
+    (b, h, i, j) of them takes the mask of (b0 + b, h0 + h, i, j), so a slice of
+    batch entries and query heads can be checked on its own."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     b_, hq_, nq, d = q.shape
     _, hkv, nk, _ = k.shape
@@ -99,16 +103,16 @@ def attn_fwd_dropout(q, k, v, p_drop: float, seed: int, scale: Optional[float] =
         for h in range(hq_):
             kh, vh = k[b, h // g, :lk], v[b, h // g, :lk]
             p, l_ = _softmax_rows(scale * (q[b, h] @ kh.T), visible_mask(rows, nq, lk, lk, causal))
-            z = keep_mask(b, h, rows, lk, seed, p_drop)
+            z = keep_mask(bh0[0] + b, bh0[1] + h, rows, lk, seed, p_drop)
             o[b, h] = (p * z * ks) @ vh
             lse[b, h] = l_
     return o, lse
 
 
 def attn_bwd_dropout(q, k, v, do, p_drop: float, seed: int, scale: Optional[float] = None,
-                     causal: bool = False, kv_lens=None):
-    """Gradients of L = sum(dO * O) for the dropout forward above.  Returns
-    (dq, dk, dv, o, lse) in float64."""
+                     causal: bool = False, kv_lens=None, bh0=(0, 0)):
+    """Gradients of L = sum(dO * O) for the dropout forward above (``bh0`` as there).
+    Returns (dq, dk, dv, o, lse) in float64."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     b_, hq_, nq, d = q.shape
     _, hkv, nk, _ = k.shape
@@ -125,7 +129,7 @@ def attn_bwd_dropout(q, k, v, do, p_drop: float, seed: int, scale: Optional[floa
         for h in range(hq_):
             kh, vh = k[b, h // g, :lk], v[b, h // g, :lk]
             p, l_ = _softmax_rows(scale * (q[b, h] @ kh.T), visible_mask(rows, nq, lk, lk, causal))
-            zs = keep_mask(b, h, rows, lk, seed, p_drop) * ks
+            zs = keep_mask(bh0[0] + b, bh0[1] + h, rows, lk, seed, p_drop) * ks
             pd = p * zs
             oh = pd @ vh
             dv[b, h // g, :lk] += pd.T @ do[b, h]

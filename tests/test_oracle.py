@@ -479,3 +479,42 @@ def test_sampled_dq_rows_equal_the_full_backward(causal):
     rows = [0, 5, 36, 17]
     part = ora.attn_bwd_dq_rows(q, k, v, do, rows, None, causal, [45, 20])
     np.testing.assert_allclose(part, full[:, :, rows], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(37, 45), (45, 37), (40, 40)], ids=["nq<nk", "nq>nk", "square"])
+def test_sampled_dkdv_rows_equal_the_full_backward(causal, shape, monkeypatch):
+    # attn_bwd is pinned by central finite differences; the sampled-key form must agree
+    # for GQA (sums over the group), kv_len (keys past it have zero gradients) and both
+    # causal alignments; a small chunk size also exercises the skipped row chunks
+    nq, nk = shape
+    rng = np.random.default_rng(32)
+    q, do = rng.standard_normal((2, 4, nq, 16)), rng.standard_normal((2, 4, nq, 16))
+    k, v = rng.standard_normal((2, 2, nk, 16)), rng.standard_normal((2, 2, nk, 16))
+    kv_lens = [nk, 20]
+    _, dk, dv = ora.attn_bwd(q, k, v, do, None, causal, kv_lens)[:3]
+    keys = [0, 1, 19, 20, nk - 1, 7, 7]
+    for chunk in (1 << 25, 64):
+        monkeypatch.setattr(ora, "_CHUNK_ELEMS", chunk)
+        pk, pv = ora.attn_bwd_dkdv_rows(q, k, v, do, keys, None, causal, kv_lens)
+        np.testing.assert_allclose(pk, dk[:, :, keys], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(pv, dv[:, :, keys], rtol=0, atol=1e-12)
+    assert np.all(pk[1, :, 3:5] == 0) and np.all(pv[1, :, 3:5] == 0)  # keys 20, nk-1 >= kv_len 20
+
+
+def test_sampled_dkdv_rows_catch_a_row_sum_over_sampled_keys_only():
+    # a plausible slip: D_i (or P) formed from the sampled key columns alone; the pin
+    # above would catch it, and so does this direct comparison with the full backward
+    rng = np.random.default_rng(33)
+    q, k, v, do = (rng.standard_normal((1, 1, 30, 8)) for _ in range(4))
+    dk = ora.attn_bwd(q, k, v, do, None, True)[1]
+    keys = [0, 3, 29]
+    s = (q[0, 0] @ k[0, 0].T) / np.sqrt(8)
+    vis = ora.visible_mask(np.arange(30), 30, 30, 30, True)
+    p, _ = ora._softmax_rows(s, vis)
+    pj = p[:, keys]
+    di_bad = np.sum(do[0, 0] * (pj @ v[0, 0, keys]), axis=-1)      # O from sampled keys only
+    dk_bad = ((pj * (do[0, 0] @ v[0, 0, keys].T - di_bad[:, None])).T @ q[0, 0]) / np.sqrt(8)
+    good = ora.attn_bwd_dkdv_rows(q, k, v, do, keys, None, True)[0][0, 0]
+    np.testing.assert_allclose(good, dk[0, 0, keys], rtol=0, atol=1e-12)
+    assert np.abs(dk_bad - dk[0, 0, keys]).max() > 1e-3

@@ -1,7 +1,8 @@
 """Pins of the oracle's dropout: the Philox4x32-10 generator against its published
 known-answer vectors, the element-to-byte mapping against scalar brute force, the
 dropout forward against the plain forward (p = 0) and against scalar loops, the
-keep rate, and the dropout backward against central finite differences.
+keep rate, the dropout backward against central finite differences, and checked
+slices (absolute batch / head offsets) against the whole computation.
 """
 
 import json
@@ -115,3 +116,23 @@ def test_dropout_is_unbiased_over_seeds():
     for seed in range(n):
         acc += dr.attn_fwd_dropout(q, k, v, 0.5, seed)[0]
     assert np.abs(acc / n - o_ref).max() < 0.1
+
+
+def test_a_slice_with_its_offsets_is_the_slice_of_the_whole():
+    # bh0 lets sampled (batch, head) slices of a large workload be checked on their own:
+    # each slice with its offsets must equal the same slice of the whole computation,
+    # and without the offsets it must not (the mask depends on the absolute indices)
+    rng = np.random.default_rng(5)
+    q, k, v, do = (rng.standard_normal((2, 3, 40, 8)) for _ in range(4))
+    seed, p = 0x1234_5678_9ABC, 0.3
+    o, lse = dr.attn_fwd_dropout(q, k, v, p, seed, None, True)
+    g = dr.attn_bwd_dropout(q, k, v, do, p, seed, None, True)
+    for b, h in ((1, 2), (0, 1)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        os_, ls = dr.attn_fwd_dropout(q[sl], k[sl], v[sl], p, seed, None, True, bh0=(b, h))
+        np.testing.assert_array_equal(os_[0, 0], o[b, h])
+        np.testing.assert_array_equal(ls[0, 0], lse[b, h])
+        gs = dr.attn_bwd_dropout(q[sl], k[sl], v[sl], do[sl], p, seed, None, True, bh0=(b, h))
+        for full, part in zip(g[:3], gs[:3]):
+            np.testing.assert_allclose(part[0, 0], full[b, h], rtol=0, atol=1e-12)
+        assert np.abs(dr.attn_fwd_dropout(q[sl], k[sl], v[sl], p, seed, None, True)[0][0, 0] - o[b, h]).max() > 1e-3
