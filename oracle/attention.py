@@ -103,20 +103,22 @@ def _softmax_rows(s: np.ndarray, vis: np.ndarray):
     """Safe softmax of each row of ``s`` over the visible entries.
 
     Subtracts the row maximum before exponentiating (study card, section 三,
-    safe softmax).  Returns (P, LSE); a row with no visible entry gets P = 0 and
-    LSE = -inf.
+    safe softmax).  Returns (P, LSE); a row with no visible entry (its maximum is
+    -inf) gets P = 0 and LSE = -inf.  Every other row follows IEEE arithmetic, so a
+    NaN among its visible scores makes its P and LSE NaN.
     """
     if s.shape[-1] == 0:  # no key exists at all
         return np.zeros(s.shape), np.full(s.shape[:-1], -np.inf)
     s = np.where(vis, s, -np.inf)
     m = np.max(s, axis=-1, keepdims=True)
-    empty = ~np.isfinite(m)
+    empty = np.isneginf(m)
     m_safe = np.where(empty, 0.0, m)
-    e = np.exp(s - m_safe)  # exp(-inf) = 0 on masked entries
+    with np.errstate(invalid="ignore"):
+        e = np.exp(s - m_safe)  # exp(-inf) = 0 on masked entries
     l = np.sum(e, axis=-1, keepdims=True)
     with np.errstate(divide="ignore", invalid="ignore"):
-        p = np.where(l > 0, e / np.where(l > 0, l, 1.0), 0.0)
-        lse = np.where(l > 0, m_safe + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+        p = np.where(empty, 0.0, e / np.where(empty, 1.0, l))
+        lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, l)))
     return p, lse[..., 0]
 
 

@@ -518,3 +518,39 @@ def test_sampled_dkdv_rows_catch_a_row_sum_over_sampled_keys_only():
     good = ora.attn_bwd_dkdv_rows(q, k, v, do, keys, None, True)[0][0, 0]
     np.testing.assert_allclose(good, dk[0, 0, keys], rtol=0, atol=1e-12)
     assert np.abs(dk_bad - dk[0, 0, keys]).max() > 1e-3
+
+
+def test_nan_inputs_reach_exactly_the_rows_that_see_them():
+    # IEEE arithmetic on the plain definition: a NaN in query row i makes row i's O and
+    # LSE NaN; a NaN in key row j makes O and LSE NaN for the rows that see j (causal:
+    # i >= j); every other row equals the result without the NaN (masked pairs and
+    # missing keys never enter a row's softmax).  A row with no visible key keeps
+    # O = 0, LSE = -inf.
+    rng = np.random.default_rng(40)
+    q, k, v = (rng.standard_normal((1, 2, 12, 8)) for _ in range(3))
+    o0, l0 = oracle.attn_fwd(q, k, v, None, True)
+    qn = q.copy()
+    qn[0, 1, 5, 3] = np.nan
+    o, l = oracle.attn_fwd(qn, k, v, None, True)
+    bad = np.zeros((2, 12), bool)
+    bad[1, 5] = True
+    assert np.all(np.isnan(o[0][bad])) and np.all(np.isnan(l[0][bad]))
+    np.testing.assert_array_equal(o[0][~bad], o0[0][~bad])
+    np.testing.assert_array_equal(l[0][~bad], l0[0][~bad])
+    kn = k.copy()
+    kn[0, 0, 7, 2] = np.nan
+    o, l = oracle.attn_fwd(q, kn, v, None, True)
+    bad = np.zeros((2, 12), bool)
+    bad[0, 7:] = True
+    assert np.all(np.isnan(o[0][bad])) and np.all(np.isnan(l[0][bad]))
+    np.testing.assert_array_equal(o[0][~bad], o0[0][~bad])
+    # a NaN key past kv_len does not exist
+    o, l = oracle.attn_fwd(q, kn, v, None, True, kv_lens=[7])
+    assert np.all(np.isfinite(o[0, :, :])) and not np.any(np.isnan(l))
+    # decode: a NaN key poisons every query head of its KV head
+    qd = rng.standard_normal((1, 4, 8))
+    kc, vc = rng.standard_normal((1, 2, 20, 8)), rng.standard_normal((1, 2, 20, 8))
+    kc[0, 1, 3, 0] = np.nan
+    od, ld = oracle.attn_decode(qd, kc, vc, [20])
+    assert np.all(np.isnan(od[0, 2:])) and np.all(np.isnan(ld[0, 2:]))
+    assert np.all(np.isfinite(od[0, :2])) and np.all(np.isfinite(ld[0, :2]))
