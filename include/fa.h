@@ -54,6 +54,13 @@
  *    read into a result (it may hold NaN).  A query row with no visible key gets
  *    O = 0 and LSE = -inf, and zero gradients.
  *  * LSE is natural-log, in the units of the scaled scores: LSE_i = m_i + ln(l_i).
+ *  * Non-finite inputs (self-test page, section G: locating NaN outputs): in fa_fwd,
+ *    fa_fwd_varlen and fa_decode, a NaN in query row i makes O_i and LSE_i NaN, and a
+ *    NaN in a key row j makes O and LSE NaN for exactly the query rows that see j;
+ *    every other row is computed as if the NaN were absent.  A NaN in a value row
+ *    reaches the O rows that see it and may reach rows of the same 64-key block that
+ *    do not (their weight 0 times NaN); LSE never depends on V.  The backward makes no
+ *    such promise: non-finite values spread through the gradient sums.
  *  * Every pointer named "device" is device memory owned by the caller; the library
  *    never allocates, frees or synchronises, keeps no mutable global state and is
  *    safe to call from several host threads.  Work is enqueued asynchronously on the

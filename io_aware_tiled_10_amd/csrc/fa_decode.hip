@@ -343,7 +343,7 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecParams p) {
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = fmaf(w, po[tid + 64 * e], acc[e]);
   }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const float inv = tot == 0.f ? 0.f : 1.f / tot;  // a NaN partial stays NaN
   if constexpr (OUT_F32) {
     float* o = static_cast<float*>(p.o) + s * p.os0 + (int64_t)hq * p.os1;
 #pragma unroll
@@ -356,7 +356,7 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecParams p) {
       o[tid + 64 * e] = static_cast<uint16_t>(pk & 0xffffu);
     }
   }
-  if (p.lse && tid == 0) p.lse[(int64_t)s * p.Hq + hq] = tot > 0.f ? M + __logf(tot) : -INFINITY;
+  if (p.lse && tid == 0) p.lse[(int64_t)s * p.Hq + hq] = tot == 0.f ? -INFINITY : M + __logf(tot);
 }
 
 template <typename K>
@@ -367,12 +367,6 @@ hipError_t launch(K kernel, dim3 grid, dim3 block, const DecParams& p, hipStream
 }
 
 }  // namespace
-
-size_t decode_workspace_bytes(int Bs, int Hq, int nsplit, int D) {
-  const size_t rows = (size_t)Bs * Hq * nsplit;
-  const size_t o_bytes = (rows * D * 4 + 255) & ~size_t(255);
-  return o_bytes + ((rows * 4 + 255) & ~size_t(255));
-}
 
 hipError_t launch_decode(const DecParams& p, int D, int out_dtype, hipStream_t stream) {
   if (p.nsplit > 0) {

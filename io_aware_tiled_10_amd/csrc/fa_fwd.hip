@@ -434,9 +434,11 @@ fwd_bf16_kernel(FwdParams p) {
   if (j + 1 < nblk) step(j + 1, Slot<2>{}, sa0, sa1, sb0, sb1, Later{});
   if (j + 2 < nblk) step(j + 2, Slot<3>{}, sb0, sb1, sa0, sa1, Later{});
 
-  // ---- epilogue: O = acc / l once (times 1 / keep with dropout); LSE = m * scale + ln(l)
+  // ---- epilogue: O = acc / l once (times 1 / keep with dropout); LSE = m * scale + ln(l).
+  // l == 0 only when no key was visible (O = 0, LSE = -inf); a NaN l (a NaN score) stays
+  // NaN in O and LSE
   const float lt = halves_sum(l);
-  const float inv = lt > 0.f ? (DROP ? p.drop_scale : 1.f) / lt : 0.f;
+  const float inv = lt == 0.f ? 0.f : (DROP ? p.drop_scale : 1.f) / lt;
   if (qi < nq) {
     const int64_t orow0 = b * p.os0 + hq * p.os1 + (qr0 + qi) * p.os2;
     if constexpr (OUT_F32) {
@@ -459,7 +461,7 @@ fwd_bf16_kernel(FwdParams p) {
                       pack_bf16(acc[d][4 * rg + 2] * inv, acc[d][4 * rg + 3] * inv)};
     }
     if (p.lse && hi == 0)
-      p.lse[b * p.lse_sb + hq * p.lse_sh + qr0 + qi] = lt > 0.f ? m * p.scale + __logf(lt) : -INFINITY;
+      p.lse[b * p.lse_sb + hq * p.lse_sh + qr0 + qi] = lt == 0.f ? -INFINITY : m * p.scale + __logf(lt);
   }
 }
 
@@ -556,13 +558,13 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdParams p) {
   }
 
   if (qi < p.Nq) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = l == 0.f ? 0.f : 1.f / l;
     float* orow = static_cast<float*>(p.o) + b * p.os0 + hq * p.os1 + (int64_t)qi * p.os2;
 #pragma unroll
     for (int d = 0; d < D; d += 4)
       *reinterpret_cast<f32x4_t*>(orow + d) =
           f32x4_t{acc[d] * inv, acc[d + 1] * inv, acc[d + 2] * inv, acc[d + 3] * inv};
-    if (p.lse) p.lse[b * p.lse_sb + hq * p.lse_sh + qi] = l > 0.f ? m * p.scale + __logf(l) : -INFINITY;
+    if (p.lse) p.lse[b * p.lse_sb + hq * p.lse_sh + qi] = l == 0.f ? -INFINITY : m * p.scale + __logf(l);
   }
 }
 

@@ -1,0 +1,81 @@
+"""Non-finite inputs on the GPU against the oracle (self-test page, section G: where
+NaN outputs come from).
+
+A NaN in query row i must make exactly O_i and LSE_i NaN; a NaN in key row j must make O
+and LSE NaN for exactly the query rows that see j; every other row must match the
+oracle computed on the same inputs (which follows IEEE arithmetic on the plain
+definition) within the usual tolerances.  The NaN elements are planted in visible
+positions of otherwise seeded inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_tiled_10_amd as fa
+import oracle
+from io_aware_tiled_10_amd import inputs
+from tests.helpers import DEV, assert_fwd_close, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def check_rows(o, lse, o_ref, lse_ref, o_is_bf16, expect_nan_rows):
+    """Rows (all leading indices of O) holding a NaN must be exactly the oracle's NaN
+    rows and the expected ones; the other rows must match the oracle."""
+    nan_gpu = np.isnan(o).any(axis=-1)
+    nan_ref = np.isnan(o_ref).any(axis=-1)
+    assert np.array_equal(nan_ref, expect_nan_rows), "the oracle's NaN rows are not the planted ones"
+    assert np.array_equal(nan_gpu, nan_ref), f"NaN rows differ: gpu {np.argwhere(nan_gpu)[:8]}"
+    assert np.array_equal(np.isnan(lse), np.isnan(lse_ref)), "NaN LSE entries differ"
+    assert np.array_equal(np.isnan(lse_ref), expect_nan_rows)
+    fin = ~expect_nan_rows
+    assert np.all(np.isfinite(o[fin])), "non-finite values in rows that see no NaN"
+    assert_fwd_close(o[fin], lse[fin], o_ref[fin], lse_ref[fin], o_is_bf16)
+    return int(nan_gpu.sum())
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["oF32", "oBF16"])
+def test_fwd_nan_reaches_exactly_the_rows_that_see_it(causal, out_dtype):
+    say(f"fwd NaN causal={causal} out={out_dtype}")
+    B, Hq, Hkv, N, D = 1, 4, 2, 300, 128
+    x = inputs.attention_inputs(B, Hq, Hkv, N, N, D, "bf16", seed=21)
+    q, k = x.q.copy(), x.k.copy()
+    q[0, 1, 5, 3] = np.nan          # query row 5 of head 1
+    k[0, 0, 170, 2] = np.nan        # key 170 of KV head 0 (query heads 0 and 1)
+    qi = q.copy()
+    o, lse = fa.fwd(to_dev(q), to_dev(k), to_dev(x.v), causal=causal, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(qi, k, x.v, None, causal)
+    expect = np.zeros((B, Hq, N), bool)
+    expect[0, 1, 5] = True
+    expect[0, 0:2, 170 if causal else 0:] = True
+    n = check_rows(to_host(o), to_host(lse), o_ref, lse_ref, out_dtype == torch.bfloat16, expect)
+    say(f"  {n} NaN rows, as planted")
+
+
+def test_decode_nan_reaches_exactly_the_heads_that_see_it():
+    say("decode NaN")
+    rng = np.random.default_rng(22)
+    lens = [3000, 4097, 900]
+    d = inputs.DecodeInputs(np.array(lens), inputs.bf16_round(rng.standard_normal((3, 8, 128), dtype=np.float32)),
+                            2, 128, seed=5)
+    lmax = 4200
+    kc = np.zeros((3, 2, lmax, 128), np.float32)
+    vc = np.zeros_like(kc)
+    for s, L in enumerate(lens):
+        kc[s, :, :L], vc[s, :, :L] = d.kv(s)
+    kc[1, 1, 2777, 9] = np.nan      # sequence 1, KV head 1: query heads 4..7
+    qn = d.q.copy()
+    qn[2, 3, 0] = np.nan            # sequence 2, query head 3
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o, lse = fa.decode(to_dev(qn), to_dev(kc), to_dev(vc), sl, max_len=lmax, split_len=1024,
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_decode(qn, kc, vc, lens)
+    expect = np.zeros((3, 8), bool)
+    expect[1, 4:] = True
+    expect[2, 3] = True
+    n = check_rows(to_host(o), to_host(lse), o_ref, lse_ref, False, expect)
+    say(f"  {n} NaN (sequence, head) rows, as planted")
