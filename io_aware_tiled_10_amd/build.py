@@ -3,7 +3,10 @@
     python -m io_aware_tiled_10_amd.build [-v]
 
 Each source under csrc/ is compiled to an object in _build/ (in parallel), then
-linked into io_aware_tiled_10_amd/libfa.so.  Always recompiles.
+linked into io_aware_tiled_10_amd/libfa.so.  A second build of the same sources with
+FA_DEBUG_SYNC (every counted wait a full wait, every barrier draining the wave's
+loads first) is linked into libfa_debugsync.so: a race canary that the tests compare
+bit for bit with the first.  Always recompiles.
 """
 
 from __future__ import annotations
@@ -20,14 +23,15 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+LIB_DEBUG_SYNC = os.path.join(PKG, "libfa_debugsync.so")
 ARCH = "gfx950"
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_quant.hip"]
 
-# The online-softmax kernels take row maxima of MFMA results; without NaN semantics the
-# compiler uses plain v_max/v_max3 instead of canonicalising every input first.  (Inputs
-# are finite; masked scores are -inf, never NaN.)
-EXTRA = {"fa_fwd.hip": ["-fno-honor-nans"], "fa_decode.hip": ["-fno-honor-nans"]}
+# Per-source extra flags.  Every kernel is built with IEEE NaN semantics: a NaN score
+# must fail the forward's block-sum test (which -fno-honor-nans folds into a plain
+# "greater than"), so NaN inputs reach the outputs that depend on them.
+EXTRA: dict = {}
 
 # Packed fp32 VALU forms are kept out of the generated code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -42,10 +46,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the ROCm toolchain is required to build libfa.so")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, verbose: bool, variant: str = "") -> str:
+    os.makedirs(os.path.join(BUILD, variant), exist_ok=True)
+    obj = os.path.join(BUILD, variant, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc(), *lang, *COMMON, *DEVICE_FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src),
+    defs = ["-DFA_DEBUG_SYNC"] if variant == "debugsync" else []
+    cmd = [hipcc(), *lang, *COMMON, *DEVICE_FLAGS, *defs, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src),
            "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -59,18 +65,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(s, v) for v in ("", "debugsync") for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
+    n = len(SOURCES)
+    _link(objs[:n], LIB, verbose)
+    _link(objs[n:], LIB_DEBUG_SYNC, verbose)
     return LIB
 
 

@@ -10,6 +10,29 @@
 #include "fa.h"
 #include "fa_internal.h"
 
+namespace fa {
+
+// Backward workspace: per query row the fp32 pair (LSE * log2 e, D_i).
+size_t bwd_workspace_bytes(int B, int Hq, int Nq, int D) {
+  (void)D;
+  return ((size_t)B * Hq * Nq * 8 + 255) & ~size_t(255);
+}
+
+void bwd_bind_workspace(BwdParams& p, void* workspace, int D) {
+  (void)D;
+  p.stats = static_cast<float*>(workspace);
+}
+
+// Decode workspace: partial O [Bs, Hq, nsplit, D] fp32, then partial LSE [Bs, Hq, nsplit]
+// fp32, each rounded up to 256 bytes.
+size_t decode_workspace_bytes(int Bs, int Hq, int nsplit, int D) {
+  const size_t rows = (size_t)Bs * Hq * nsplit;
+  const size_t o_bytes = (rows * D * 4 + 255) & ~size_t(255);
+  return o_bytes + ((rows * 4 + 255) & ~size_t(255));
+}
+
+}  // namespace fa
+
 namespace {
 
 constexpr int kMaxHeads = 1 << 16;

@@ -772,16 +772,6 @@ hipError_t launch_all(BwdParams p, hipStream_t stream) {
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int B, int Hq, int Nq, int D) {
-  (void)D;
-  return ((size_t)B * Hq * Nq * 8 + 255) & ~size_t(255);
-}
-
-void bwd_bind_workspace(BwdParams& p, void* workspace, int D) {
-  (void)D;
-  p.stats = static_cast<float*>(workspace);
-}
-
 hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t stream) {
   if (p.drop_t > 0)
     return D == 128 ? launch_all<128, true>(p, stream) : launch_all<64, true>(p, stream);

@@ -141,7 +141,16 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, u
 
 // Wait until at most N vector-memory operations of this wave are outstanding; also a
 // compiler barrier for memory accesses.
+//
+// FA_DEBUG_SYNC builds (a race canary): every counted wait waits for all of the wave's
+// outstanding operations, and every fence-free barrier first drains the wave's loads and
+// LDS reads.  The arithmetic is unchanged, so such a build must give the same bits; a
+// wait count that were too loose would show up as a difference.
+#ifdef FA_DEBUG_SYNC
+#define FA_WAIT_VMCNT(N) asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
+#else
 #define FA_WAIT_VMCNT(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
+#endif
 #define FA_WAIT_LGKMCNT0() asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory")
 // FA_WAIT_VMCNT for a compile-time count (the counts the ring pipelines use).
 template <int N>
@@ -191,7 +200,11 @@ __device__ __forceinline__ bool dropout_keep(uint32_t word, int byte, uint32_t t
 // Workgroup barrier without the memory fence __syncthreads() adds (which waits for every
 // outstanding load, ring prefetches included).  Callers order LDS themselves: each wave
 // waits for its own ring loads (FA_WAIT_VMCNT) and LDS reads (lgkmcnt) before it.
+#ifdef FA_DEBUG_SYNC
+#define FA_BARRIER() asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory")
+#else
 #define FA_BARRIER() asm volatile("s_barrier" ::: "memory")
+#endif
 
 // gfx950 transposing LDS read (ds_read_b64_tr_b16) of 4 bf16 values per lane.  Within
 // each group of 16 lanes, let M be the 16 x 4 matrix whose row i is the 8 bytes at lane
@@ -223,7 +236,11 @@ __device__ __forceinline__ void lds_wait_tr(u32x2_t& a, u32x2_t& b, u32x2_t& c, 
 template <int N>
 __device__ __forceinline__ void lds_wait_tr(u32x2_t& a, u32x2_t& b, u32x2_t& c, u32x2_t& d) {
   static_assert(N >= 0 && N <= 15, "lgkmcnt holds 0..15");
+#ifdef FA_DEBUG_SYNC
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d)::"memory");
+#else
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N) : "memory");
+#endif
 }
 // LDS byte address of a pointer into __shared__ memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

@@ -1,0 +1,159 @@
+"""Out-of-bounds write detection: every output and workspace is placed inside a larger
+buffer filled with a sentinel byte pattern, with a guard region before and after it and
+(for row-strided outputs) a gap after every row; after the call every sentinel byte must
+be intact, and the values must equal those of the plain contiguous call.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_tiled_10_amd as fa
+from io_aware_tiled_10_amd import inputs
+from tests.helpers import DEV, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0xA5
+GUARD = 4096  # bytes before and after each buffer (keeps 16-byte alignment)
+
+
+class Guarded:
+    """A tensor of `shape` / `dtype` whose rows (last dim) are `gap` elements apart,
+    inside a sentinel-filled byte buffer with GUARD bytes on both sides."""
+
+    def __init__(self, shape, dtype, gap=0):
+        esz = torch.empty((), dtype=dtype).element_size()
+        self.padded = tuple(shape[:-1]) + (shape[-1] + gap,)
+        n = int(np.prod(self.padded)) * esz
+        self.buf = torch.full((n + 2 * GUARD,), SENT, dtype=torch.uint8, device=DEV)
+        inner = self.buf[GUARD:GUARD + n].view(dtype).view(self.padded)
+        self.t = inner[..., :shape[-1]]
+        self.gap = gap
+
+    def intact(self) -> bool:
+        torch.cuda.synchronize()
+        ok = bool((self.buf[:GUARD] == SENT).all()) and bool((self.buf[-GUARD:] == SENT).all())
+        if self.gap:
+            inner = self.buf[GUARD:-GUARD].view(self.t.dtype).view(self.padded)
+            gaps = inner[..., self.t.shape[-1]:].contiguous().view(torch.uint8)
+            ok = ok and bool((gaps == SENT).all())
+        return ok
+
+
+def bits_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["oBF16", "oF32"])
+def test_fwd_writes_nothing_outside_o_and_lse(out_dtype):
+    say(f"guards fwd {out_dtype}")
+    B, Hq, Hkv, N, D = 3, 4, 2, 300, 128
+    x = inputs.attention_inputs(B, Hq, Hkv, N, N, D, "bf16", seed=41)
+    q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
+    kl = torch.tensor([300, 0, 77], dtype=torch.int32, device=DEV)  # one batch entry sees no key
+    for causal in (False, True):
+        go, gl = Guarded((B, Hq, N, D), out_dtype, gap=24), Guarded((B, Hq, N), torch.float32)
+        fa.fwd(q, k, v, causal=causal, kv_lens=kl, out=go.t, lse_out=gl.t)
+        ref = fa.fwd(q, k, v, causal=causal, kv_lens=kl, out_dtype=out_dtype)
+        assert go.intact() and gl.intact(), causal
+        assert bits_equal(go.t, ref[0]) and bits_equal(gl.t, ref[1])
+
+
+def test_fwd_f32_writes_nothing_outside_o_and_lse():
+    say("guards fwd fp32")
+    x = inputs.attention_inputs(1, 2, 2, 257, 257, 64, "fp32", seed=42)
+    q, k, v = (to_dev(a, torch.float32) for a in (x.q, x.k, x.v))
+    go, gl = Guarded((1, 2, 257, 64), torch.float32, gap=16), Guarded((1, 2, 257), torch.float32)
+    fa.fwd(q, k, v, causal=True, out=go.t, lse_out=gl.t)
+    ref = fa.fwd(q, k, v, causal=True)
+    assert go.intact() and gl.intact()
+    assert bits_equal(go.t, ref[0]) and bits_equal(gl.t, ref[1])
+
+
+@pytest.mark.parametrize("drop", [0.0, 0.2], ids=["plain", "dropout"])
+def test_bwd_writes_nothing_outside_the_gradients_and_workspace(drop):
+    say(f"guards bwd p={drop}")
+    B, Hq, Hkv, N, D = 2, 4, 2, 300, 128
+    x = inputs.attention_inputs(B, Hq, Hkv, N, N, D, "bf16", seed=43, with_grad=True)
+    q, k, v, do = to_dev(x.q), to_dev(x.k), to_dev(x.v), to_dev(x.do)
+    kl = torch.tensor([300, 130], dtype=torch.int32, device=DEV)
+    fwd = (lambda: fa.fwd(q, k, v, causal=True, kv_lens=kl)) if drop == 0 else \
+        (lambda: fa.fwd_dropout(q, k, v, drop, 7, causal=True, kv_lens=kl))
+    o, lse = fwd()
+    need = fa.binding.bwd_workspace_bytes(q, k, v)
+    gq, gk, gv = (Guarded(t.shape, torch.bfloat16, gap=40) for t in (q, k, v))
+    gw = Guarded((need,), torch.uint8)
+    if drop == 0:
+        fa.bwd(q, k, v, o, do, lse, causal=True, kv_lens=kl, workspace=gw.t, grads=(gq.t, gk.t, gv.t))
+        ref = fa.bwd(q, k, v, o, do, lse, causal=True, kv_lens=kl)
+    else:
+        fa.bwd_dropout(q, k, v, o, do, lse, drop, 7, causal=True, kv_lens=kl, workspace=gw.t,
+                       grads=(gq.t, gk.t, gv.t))
+        ref = fa.bwd_dropout(q, k, v, o, do, lse, drop, 7, causal=True, kv_lens=kl)
+    for g in (gq, gk, gv, gw):
+        assert g.intact()
+    for a, b in zip((gq.t, gk.t, gv.t), ref):
+        assert bits_equal(a, b)
+
+
+def test_decode_writes_nothing_outside_o_lse_and_workspace():
+    say("guards decode")
+    rng = np.random.default_rng(44)
+    lens = [1, 2048, 2049, 5000, 0]
+    d = inputs.DecodeInputs(np.array(lens), inputs.bf16_round(rng.standard_normal((5, 8, 128), dtype=np.float32)),
+                            2, 128, seed=6)
+    lmax = 5000
+    kc = torch.zeros((5, 2, lmax, 128), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    for s, L in enumerate(lens):
+        if L:
+            kk, vv = d.kv(s)
+            kc[s, :, :L], vc[s, :, :L] = to_dev(kk), to_dev(vv)
+    q = to_dev(d.q)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    import ctypes
+    for out_dtype in (torch.bfloat16, torch.float32):
+        go, gl = Guarded((5, 8, 128), out_dtype, gap=8), Guarded((5, 8), torch.float32)
+        a = fa.binding.decode_args(q, kc, vc, sl, go.t, gl.t, lmax, 1024, None)
+        gw = Guarded((fa.lib().fa_decode_workspace_bytes(ctypes.byref(a)),), torch.uint8)
+        fa.decode(q, kc, vc, sl, max_len=lmax, split_len=1024, workspace=gw.t, out=go.t, lse_out=gl.t)
+        ref = fa.decode(q, kc, vc, sl, max_len=lmax, split_len=1024, out_dtype=out_dtype)
+        for g in (go, gl, gw):
+            assert g.intact()
+        assert bits_equal(go.t, ref[0]) and bits_equal(gl.t, ref[1])
+
+
+def test_varlen_writes_no_row_past_the_packed_total():
+    say("guards varlen")
+    lens = [70, 0, 300, 1, 129]
+    x = inputs.varlen_inputs(lens, lens, 4, 2, 128, "bf16", seed=45)
+    total, extra = sum(lens), 50
+    pad = lambda a: np.concatenate([a, np.zeros((extra,) + a.shape[1:], np.float32)])
+    q, k, v = to_dev(pad(x.q)), to_dev(pad(x.k)), to_dev(pad(x.v))
+    cu = torch.from_numpy(x.cu_q).to(DEV)
+    go, gl = Guarded((total + extra, 4, 128), torch.bfloat16, gap=8), Guarded((4, total + extra), torch.float32)
+    fa.fwd_varlen(q, k, v, cu, cu, max(lens), causal=True, out=go.t, lse_out=gl.t)
+    ref = fa.fwd_varlen(q[:total], k[:total], v[:total], cu, cu, max(lens), causal=True)
+    assert go.intact() and gl.intact()
+    torch.cuda.synchronize()
+    assert bool((go.t[total:].contiguous().view(torch.uint8) == SENT).all()), "rows past the total were written"
+    assert bool((gl.t[:, total:].contiguous().view(torch.uint8) == SENT).all())
+    assert bits_equal(go.t[:total], ref[0]) and bits_equal(gl.t[:, :total], ref[1])
+
+
+def test_fp8_quantise_and_forward_write_nothing_outside_their_outputs():
+    say("guards fp8")
+    x = inputs.attention_inputs(1, 4, 2, 200, 200, 128, "bf16", seed=46)
+    q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
+    gc, gs = Guarded(q.shape, torch.uint8, gap=16), Guarded((1, 4, 4), torch.float32)
+    fa.quantize_fp8(q, out=gc.t, scales_out=gs.t)
+    q8, qs = fa.quantize_fp8(q)
+    k8, ks = fa.quantize_fp8(k)
+    assert gc.intact() and gs.intact()
+    assert bits_equal(gc.t, q8) and bits_equal(gs.t, qs)
+    go, gl = Guarded(q.shape, torch.bfloat16, gap=8), Guarded((1, 4, 200), torch.float32)
+    fa.fwd_fp8(q8, qs, k8, ks, v, causal=True, out=go.t, lse_out=gl.t)
+    ref = fa.fwd_fp8(q8, qs, k8, ks, v, causal=True)
+    assert go.intact() and gl.intact()
+    assert bits_equal(go.t, ref[0]) and bits_equal(gl.t, ref[1])
