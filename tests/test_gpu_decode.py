@@ -74,7 +74,7 @@ def test_decode_is_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_decode_full_size_c5_sampled_sequences():
+def test_decode_full_size_c5_every_sequence():
     # 64 sequences, Hq 32, Hkv 8, D 128, lengths U[1024, 32768], chunks of 2048
     say("decode full c5")
     d = inputs.decode_inputs(64, 32, 8, 128, 1024, 32768, seed=0)
@@ -85,7 +85,7 @@ def test_decode_full_size_c5_sampled_sequences():
     o, lse = fa.decode(q, kc, vc, sl, max_len=lmax, split_len=2048)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    seqs = [int(np.argmin(d.seq_lens)), int(np.argmax(d.seq_lens)), 0, 17, 63]
+    seqs = list(range(64))
     o_ref, lse_ref = oracle_decode(d, seqs)
     assert_fwd_close(to_host(o[seqs]), to_host(lse[seqs]), o_ref, lse_ref, True)
 

@@ -81,3 +81,29 @@ def test_zero_dropout_is_the_plain_forward_and_seeds_matter():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     assert torch.equal(c1[0], c2[0]) and not torch.equal(c1[0], c3[0])
     assert torch.equal(c1[1], b[1])  # the log-sum-exp is that of the undropped scores
+
+
+def test_dropout_full_size_c4_sampled_heads():
+    # the timed dropout workload: B2 H16 N4096 D128 causal, p = 0.1, launched as the
+    # benchmark launches it; two whole (batch, head) slices against the oracle, which
+    # draws each slice's mask at its absolute (batch, head) index
+    say("dropout full c4")
+    B, H, N, D, p = 2, 16, 4096, 128, 0.1
+    seed = 0x5EED
+    x = inputs.attention_inputs(B, H, H, N, N, D, "bf16", seed=0, with_grad=True)
+    q, k, v, do = to_dev(x.q), to_dev(x.k), to_dev(x.v), to_dev(x.do)
+    o32, lse32 = fa.fwd_dropout(q, k, v, p, seed, causal=True, out_dtype=torch.float32)
+    o, lse = fa.fwd_dropout(q, k, v, p, seed, causal=True)
+    dq, dk, dv = fa.bwd_dropout(q, k, v, o, do, lse, p, seed, causal=True)
+    torch.cuda.synchronize()
+    for t in (o, dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    for b, h in ((0, 0), (1, 11)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = odr.attn_bwd_dropout(x.q[sl], x.k[sl], x.v[sl], x.do[sl], p, seed, None, True, bh0=(b, h))
+        assert_fwd_close(to_host(o32[sl]), to_host(lse32[sl]), ref[3], ref[4], False,
+                         tol_o=2.0 ** -8 * odr.keep_scale(p) * float(np.abs(x.v[sl]).max()) + 1e-3)
+        for nm, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+            e = rel_l2(to_host(g[sl]), r)
+            say(f"  b{b} h{h} {nm} rel-L2 {e:.3e}")
+            assert e <= 2e-2, (b, h, nm, e)

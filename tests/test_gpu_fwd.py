@@ -169,10 +169,29 @@ def test_fwd_empty_key_set_gives_zero_and_neg_inf():
 # --------------------------------------------------------------------------------------
 
 FULL = [
-    ("c2_noncausal", 4, 16, 16, 2048, 128, False),
-    ("c2_causal", 4, 16, 16, 2048, 128, True),
     ("c3_gqa_causal_16k", 1, 32, 8, 16384, 128, True),
 ]
+WHOLE = [
+    ("c2_noncausal", 4, 16, 16, 2048, 128, False),
+    ("c2_causal", 4, 16, 16, 2048, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", WHOLE, ids=[c[0] for c in WHOLE])
+def test_fwd_full_size_every_row(case):
+    # B4 H16 N2048 D128: the oracle covers every output element in a few seconds
+    name, B, Hq, Hkv, N, D, causal = case
+    say(f"fwd whole {name}")
+    x = inputs.attention_inputs(B, Hq, Hkv, N, N, D, "bf16", seed=0)
+    q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
+    o, lse = fa.fwd(q, k, v, causal=causal)              # bf16 O, as timed
+    o32, lse32 = fa.fwd(q, k, v, causal=causal, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(x.q, x.k, x.v, None, causal)
+    e32 = assert_fwd_close(to_host(o32), to_host(lse32), o_ref, lse_ref, False)
+    e16 = assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, True)
+    say(f"  max|dO| fp32 out {e32:.3e}, bf16 out {e16:.3e}")
+    assert torch.equal(lse, lse32)
 
 
 @pytest.mark.parametrize("case", FULL, ids=[c[0] for c in FULL])
