@@ -25,9 +25,19 @@ Throughput counts only matmul FLOPs over the (query, key) pairs that exist:
 backward (five products, one of them the recompute of S).  Decode bandwidth counts
 each valid cached K/V byte once plus q and O.
 
+Outside the step (not in `value`), the bench also times the two short forwards,
+B4 H16 N2048 D128 bf16 non-causal and causal, and the fp32 forward B1 H2 N256 D64.
+
 Prints one JSON line.  The CPU baseline times the fp64 oracle on bounded samples of
 each leg's workload (whole query heads, (batch, head) slices, sequences) on the host
-cores and reports the step-level rate those samples imply.  `roofline`
+cores and reports the step-level rate those samples imply.  The same oracle results
+are compared with the GPU's outputs of one untimed call per leg made after the timed
+steps (`parity`: forward O max-abs <= 1e-2 plus half a bf16 ulp of the reference and
+LSE <= 1e-3, backward relative L2 <= 2e-2 per tensor and slice, decode as the forward;
+the short forwards are checked on two whole (batch, head) slices each); the run exits
+with status 3 if any sample fails.  `value` is the credited matmul FLOPs of the three
+legs (the decode's Q K^T and P V included, at 4*D per cached key and query head) over
+the step time.  `roofline`
 describes the forward kernel (the largest share of the step): achieved = credited
 FLOPs / mean HIP-event duration of its launch; `traffic` = HBM bytes per launch from
 the committed counter summary (FETCH_SIZE and WRITE_SIZE scaled by their readings
@@ -62,8 +72,11 @@ DEV = "cuda:0"
 FWD_CFG = dict(B=1, Hq=32, Hkv=8, N=16384, D=128, causal=True)
 BWD_CFG = dict(B=2, H=16, N=4096, D=128, causal=True)
 DEC_CFG = dict(Bs=64, Hq=32, Hkv=8, D=128, lo=1024, hi=32768, split=2048, lmax=32768)
-AUX_CFGS = {"fwd_b4h16n2048_noncausal": dict(B=4, Hq=16, Hkv=16, N=2048, D=128, causal=False),
-            "fwd_b4h16n2048_causal": dict(B=4, Hq=16, Hkv=16, N=2048, D=128, causal=True)}
+# timed outside the step by default: the short forwards and the fp32 forward
+SHORT_CFGS = {"fwd_b4h16n2048_noncausal": dict(B=4, Hq=16, Hkv=16, N=2048, D=128, causal=False),
+              "fwd_b4h16n2048_causal": dict(B=4, Hq=16, Hkv=16, N=2048, D=128, causal=True),
+              "fwd_f32_b1h2n256d64": dict(B=1, Hq=2, Hkv=2, N=256, D=64, causal=False, dtype="fp32")}
+TOL_O, TOL_LSE, TOL_GRAD = 1e-2, 1e-3, 2e-2
 # packed variable-length prefill: 32 sequences of U[256, 4096] rows (seed 0), causal GQA
 VARLEN_CFG = dict(B=32, lo=256, hi=4096, Hq=32, Hkv=8, D=128, causal=True)
 # GQA backward at the long-sequence forward's shape
@@ -101,8 +114,11 @@ def bf16_dev(x: np.ndarray) -> torch.Tensor:
 class FwdLeg:
     def __init__(self, cfg, seed=0):
         self.cfg = cfg
-        x = inputs.attention_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["N"], cfg["D"], "bf16", seed)
-        self.q, self.k, self.v = bf16_dev(x.q), bf16_dev(x.k), bf16_dev(x.v)
+        dt = cfg.get("dtype", "bf16")
+        x = inputs.attention_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["N"], cfg["D"], dt, seed)
+        self.x = x
+        dev = bf16_dev if dt == "bf16" else (lambda a: torch.from_numpy(a).to(DEV))
+        self.q, self.k, self.v = dev(x.q), dev(x.k), dev(x.v)
         self.o = torch.empty_like(self.q)
         self.lse = torch.empty(self.q.shape[:3], dtype=torch.float32, device=DEV)
         self.flops = 4 * cfg["D"] * pairs(cfg["N"], cfg["N"], cfg["causal"]) * cfg["B"] * cfg["Hq"]
@@ -265,48 +281,112 @@ def time_aux(leg, stream, reps=20):
 # CPU baseline: the oracle as it stands, on bounded samples of each leg's workload
 # ------------------------------------------------------------------------------------
 
-def _host_threads_and_model():
+def _host_cpu():
+    """Host threads the oracle's BLAS uses, cores this process may run on, CPU model."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
-    cpu_model = ""
+        blas = 1
     try:
-        for ln in open("/proc/cpuinfo"):
-            if ln.startswith("model name"):
-                cpu_model = ln.split(":", 1)[1].strip()
-                break
+        affinity = len(os.sched_getaffinity(0))
     except OSError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    model = ""
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for ln in out.splitlines():
+            if ln.strip().startswith("Model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except Exception:  # pragma: no cover
         pass
-    return int(threads), cpu_model
+    if not model:
+        try:
+            for ln in open("/proc/cpuinfo"):
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+        except OSError:  # pragma: no cover
+            pass
+    return int(blas), int(affinity), model
 
 
-def cpu_baseline(budgets=(9.0, 4.0, 3.0)):
+def _half_ulp_bf16(x: np.ndarray) -> np.ndarray:
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 2.0 ** -134)
+
+
+class _Parity:
+    """Running worst errors of one leg's samples against the oracle."""
+
+    def __init__(self, kind: str):
+        self.kind, self.n, self.ok = kind, 0, True
+        self.worst = {}
+
+    def _max(self, k, v):
+        self.worst[k] = max(self.worst.get(k, 0.0), float(v))
+
+    def fwd(self, o, lse, o_ref, lse_ref, o_bf16: bool):
+        self.n += 1
+        finite = bool(np.all(np.isfinite(o)) and np.all(np.isfinite(lse)))
+        err = np.abs(o - o_ref)
+        excess = float((err - (TOL_O + (_half_ulp_bf16(o_ref) if o_bf16 else 0.0))).max())
+        el = float(np.abs(lse - lse_ref).max())
+        self._max("o_max_abs", err.max())
+        self._max("lse_max_abs", el)
+        self.worst["o_bound_excess"] = max(self.worst.get("o_bound_excess", -1.0), excess)
+        self.ok &= finite and excess <= 0 and el <= TOL_LSE
+
+    def grads(self, got, ref):
+        self.n += 1
+        for nm, g, r in zip(("dq", "dk", "dv"), got, ref):
+            g, r = np.asarray(g, np.float64), np.asarray(r, np.float64)
+            e = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300))
+            self._max(f"{nm}_rel_l2", e)
+            self.ok &= bool(np.all(np.isfinite(g))) and e <= TOL_GRAD
+
+    def record(self, samples: str):
+        return {"samples": samples, "checked": self.n,
+                **{k: float(f"{v:.4g}") for k, v in self.worst.items()}, "pass": bool(self.ok and self.n > 0)}
+
+
+def cpu_baseline(gpu=None, budgets=(9.0, 4.0, 3.0)):
     """The fp64 oracle timed on the host cores, leg by leg, on bounded samples of the
     step's own workloads: whole query heads of the forward, whole (batch, head) slices
     of the backward, whole sequences of the decode (each until its time budget in
     seconds runs out; input generation is not timed).  `value` is the step's credited
-    FLOPs over the time the oracle would take for the whole step at those rates."""
+    FLOPs over the time the oracle would take for the whole step at those rates.
+
+    ``gpu``: host copies of the GPU's outputs for the same workloads (one untimed call
+    per leg after the timed steps); each oracle result is then also compared with them
+    (outside the timed calls).  Returns (baseline record, parity record or None)."""
     import oracle
 
     rates, samples = {}, {}
+    par = {k: _Parity(k) for k in ("fwd", "bwd", "decode")} if gpu is not None else None
     # forward: query heads of B1 Hq32 Hkv8 N16384 D128 causal
     cfg = FWD_CFG
     x = inputs.attention_inputs(1, cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["N"], cfg["D"], "bf16", 0)
     G = cfg["Hq"] // cfg["Hkv"]
     per_head = 4 * cfg["D"] * pairs(cfg["N"], cfg["N"], cfg["causal"])
     step_flops = {"fwd": per_head * cfg["Hq"]}
-    done, t0 = 0, time.perf_counter()
-    while done < cfg["Hq"]:
-        h = done
-        oracle.attn_fwd(x.q[:, h:h + 1], x.k[:, h // G:h // G + 1], x.v[:, h // G:h // G + 1], None, True)
+    done, el = 0, 0.0
+    # heads spread over the KV groups: 0, 31, 9, 22, ... (every group within the first 8)
+    order = [0, 31, 9, 22, 5, 18, 27, 14] + [h for h in range(32) if h not in (0, 31, 9, 22, 5, 18, 27, 14)]
+    while done < cfg["Hq"] and el < budgets[0]:
+        h = order[done]
+        t0 = time.perf_counter()
+        o_ref, lse_ref = oracle.attn_fwd(x.q[:, h:h + 1], x.k[:, h // G:h // G + 1], x.v[:, h // G:h // G + 1],
+                                         None, True)
+        el += time.perf_counter() - t0
         done += 1
-        if time.perf_counter() - t0 >= budgets[0]:
-            break
-    el = time.perf_counter() - t0
+        if par is not None:
+            par["fwd"].fwd(gpu["fwd_o"][:, h:h + 1], gpu["fwd_lse"][:, h:h + 1], o_ref, lse_ref, True)
     rates["fwd"] = per_head * done / el
-    samples["fwd"] = f"{done} of 32 query heads ({done * per_head / 1e9:.1f} GFLOP, {el:.1f} s)"
+    samples["fwd"] = f"{done} of 32 query heads, all rows ({done * per_head / 1e9:.1f} GFLOP, {el:.1f} s)"
     del x
     # backward: (batch, head) slices of B2 H16 N4096 D128 causal
     cfg = BWD_CFG
@@ -314,15 +394,16 @@ def cpu_baseline(budgets=(9.0, 4.0, 3.0)):
     x = inputs.attention_inputs(B, H, H, N, N, D, "bf16", 0, with_grad=True)
     per_head = 10 * D * pairs(N, N, cfg["causal"])
     step_flops["bwd"] = per_head * B * H
-    done, t0 = 0, time.perf_counter()
-    while done < B * H:
-        b, h = divmod(done, H)
+    done, el = 0, 0.0
+    while done < B * H and el < budgets[1]:
+        b, h = divmod((13 * done) % (B * H), H)  # a fixed permutation of the slices
         sl = (slice(b, b + 1), slice(h, h + 1))
-        oracle.attn_bwd(x.q[sl], x.k[sl], x.v[sl], x.do[sl], None, True)
+        t0 = time.perf_counter()
+        ref = oracle.attn_bwd(x.q[sl], x.k[sl], x.v[sl], x.do[sl], None, True)
+        el += time.perf_counter() - t0
         done += 1
-        if time.perf_counter() - t0 >= budgets[1]:
-            break
-    el = time.perf_counter() - t0
+        if par is not None:
+            par["bwd"].grads([gpu[f"bwd_{n}"][sl] for n in ("dq", "dk", "dv")], ref[:3])
     rates["bwd"] = per_head * done / el
     samples["bwd"] = f"{done} of {B * H} (batch, head) slices ({done * per_head / 1e9:.1f} GFLOP, {el:.1f} s)"
     del x
@@ -336,21 +417,40 @@ def cpu_baseline(budgets=(9.0, 4.0, 3.0)):
         k, v = d.kv(done)
         L = int(d.seq_lens[done])
         t0 = time.perf_counter()
-        oracle.attn_decode(d.q[done:done + 1], k[None], v[None], [L])
+        o_ref, lse_ref = oracle.attn_decode(d.q[done:done + 1], k[None], v[None], [L])
         el += time.perf_counter() - t0
+        if par is not None:
+            par["decode"].fwd(gpu["dec_o"][done:done + 1], gpu["dec_lse"][done:done + 1], o_ref, lse_ref, True)
         done, keys = done + 1, keys + L
     rates["decode"] = fl_per_key * keys / el
     samples["decode"] = (f"{done} of 64 sequences ({keys} cached positions, "
                          f"{2 * cfg['Hkv'] * cfg['D'] * 2 * keys / el / 1e9:.2f} GB/s of K/V, {el:.1f} s)")
 
-    threads, cpu_model = _host_threads_and_model()
+    blas, affinity, cpu_model = _host_cpu()
     t_step = sum(step_flops[k] / rates[k] for k in step_flops)
-    return {"value": round(sum(step_flops.values()) / t_step / 1e12, 6), "unit": "TFLOP/s",
-            "cores": threads, "kind": "oracle", "cpu_model": cpu_model,
+    base = {"value": round(sum(step_flops.values()) / t_step / 1e12, 6), "unit": "TFLOP/s",
+            "cores": blas, "kind": "oracle", "blas_threads": blas, "affinity_cores": affinity,
+            "cpu_model": cpu_model,
             "legs_tflops": {k: round(r / 1e12, 6) for k, r in rates.items()},
             "est_s_per_step": round(t_step, 1),
             "sample": "fp64 numpy oracle on the step's workloads, timed per leg on bounded samples: "
                       + "; ".join(f"{k}: {v}" for k, v in samples.items())}
+    parity = None
+    if par is not None:
+        parity = {k: par[k].record(samples[k]) for k in par}
+        if "short" in gpu:
+            ps = _Parity("short")
+            for name, (leg, o, lse) in gpu["short"].items():
+                cfg = leg.cfg
+                for b, h in ((0, 0), (cfg["B"] - 1, cfg["Hq"] - 1)):
+                    sl = (slice(b, b + 1), slice(h, h + 1))
+                    o_ref, lse_ref = oracle.attn_fwd(leg.x.q[sl], leg.x.k[sl], leg.x.v[sl], None, cfg["causal"])
+                    ps.fwd(o[sl], lse[sl], o_ref, lse_ref, cfg.get("dtype", "bf16") == "bf16")
+            parity["short_fwd"] = ps.record("two whole (batch, head) slices of each of " + ", ".join(gpu["short"]))
+        parity["tolerances"] = {"o_max_abs": f"{TOL_O} (+ half a bf16 ulp of the reference for bf16 O)",
+                                "lse_max_abs": TOL_LSE, "grad_rel_l2": TOL_GRAD}
+        parity["pass"] = all(v["pass"] for k, v in parity.items() if isinstance(v, dict) and "pass" in v)
+    return base, parity
 
 
 def ceilings():
@@ -471,10 +571,13 @@ def main():
                     help="timed steps (64 steps of the default legs take about 0.2 s)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="fwd,bwd,decode")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle on the host (and with it the parity check)")
+    ap.add_argument("--no-short", action="store_true",
+                    help="skip the short forwards timed outside the step")
     ap.add_argument("--aux", action="store_true",
-                    help="also time the B4 H16 N2048 forwards, the packed variable-length forward and "
-                         "the paged-cache decode (outside the step)")
+                    help="also time dropout, the FP8 forward, the GQA backward, the packed "
+                         "variable-length forward and the paged-cache decode (outside the step)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--ceilings", action="store_true",
@@ -549,16 +652,40 @@ def main():
                         "algorithmic_bytes": int(leg.bytes)})
         out_legs[n] = rec
 
-    if args.aux:
-        def flops_rec(leg, ms):
-            tf = leg.flops / (ms * 1e-3) / 1e12
-            return {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                    "in_step": False}
+    # one untimed call per leg; host copies of its outputs for the parity check
+    gpu_out = {}
+    if not args.no_cpu_baseline:
+        for n, leg in legs.items():
+            leg.run()
+        torch.cuda.synchronize()
+        host = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+        if "fwd" in legs:
+            gpu_out["fwd_o"], gpu_out["fwd_lse"] = host(legs["fwd"].o), host(legs["fwd"].lse)
+        if "bwd" in legs:
+            for nm, t in zip(("dq", "dk", "dv"), legs["bwd"].grads):
+                gpu_out[f"bwd_{nm}"] = host(t)
+        if "decode" in legs:
+            gpu_out["dec_o"], gpu_out["dec_lse"] = host(legs["decode"].o), host(legs["decode"].lse)
 
-        for name, cfg in AUX_CFGS.items():
+    def flops_rec(leg, ms):
+        tf = leg.flops / (ms * 1e-3) / 1e12
+        return {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                "in_step": False}
+
+    if not args.no_short:
+        short = {}
+        for name, cfg in SHORT_CFGS.items():
             leg = FwdLeg(cfg)
-            out_legs[name] = flops_rec(leg, time_aux(leg, stream))
-            del leg
+            out_legs[name] = flops_rec(leg, time_aux(leg, stream, reps=20 if cfg["N"] > 1024 else 200))
+            leg.run()  # untimed call for the parity check
+            torch.cuda.synchronize()
+            short[name] = (leg, leg.o.detach().float().cpu().numpy().astype(np.float64),
+                           leg.lse.detach().cpu().numpy().astype(np.float64))
+            leg.q = leg.k = leg.v = leg.o = None
+        if not args.no_cpu_baseline:
+            gpu_out["short"] = short
+
+    if args.aux:
         fl = legs["fwd"] if "fwd" in legs else FwdLeg(FWD_CFG)
         bl = legs["bwd"] if "bwd" in legs else BwdLeg(BWD_CFG)
         dl = DropoutLegs(fl, bl)
@@ -617,10 +744,10 @@ def main():
     if args.ceilings:
         log("measuring library GEMM / streaming-read ceilings ...")
         ceil = ceilings()
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
-        log("timing the oracle on the host ...")
-        cpu = cpu_baseline()
+        log("timing the oracle on the host and checking the GPU outputs against it ...")
+        cpu, parity = cpu_baseline(gpu_out if legs else None)
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -629,10 +756,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": "one step = fwd B1 Hq32 Hkv8 N16384 D128 causal + bwd B2 H16 N4096 D128 "
                                "causal + split-KV decode 64 seqs Hq32 Hkv8 D128 L~U[1024,32768] split 2048",
-                   "legs": list(legs), "seed": 0, "global_batch": None, "parallelism": "single GPU"},
+                   "legs": list(legs), "seed": 0, "global_batch": None, "parallelism": "single GPU",
+                   "value": "credited matmul FLOPs of the step's three legs (4*D per visible pair forward, "
+                            "10*D backward, 4*D per cached key and query head decode) / step time; the "
+                            "per-leg rates and fractions of peak are under legs"},
         "legs": out_legs,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     if ceil is not None:
         line["ceilings"] = ceil
@@ -640,6 +771,9 @@ def main():
     line["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                       "hip_runtime": getattr(torch.version, "hip", None), "cus": props.multi_processor_count}
     print(json.dumps(line), flush=True)
+    if parity is not None and not parity["pass"]:
+        log("parity check FAILED: " + json.dumps(parity))
+        sys.exit(3)
 
 
 if __name__ == "__main__":
