@@ -36,6 +36,8 @@
  *                    Pages: self-test page, section F (why paged attention or a decode
  *                    kernel is still needed); interview answer, 高频追问 2 (blocked decode
  *                    reading the paged KV blocks directly).
+ *   fa_decode_noalloc  fa_decode with its partials in a static per-device array, for
+ *                    callers that cannot allocate device memory.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -62,8 +64,9 @@
  *    do not (their weight 0 times NaN); LSE never depends on V.  The backward makes no
  *    such promise: non-finite values spread through the gradient sums.
  *  * Every pointer named "device" is device memory owned by the caller; the library
- *    never allocates, frees or synchronises, keeps no mutable global state and is
- *    safe to call from several host threads.  Work is enqueued asynchronously on the
+ *    never allocates, frees or synchronises, keeps no mutable global state (apart from
+ *    fa_decode_noalloc's static per-device array, described there) and is safe to call
+ *    from several host threads.  Work is enqueued asynchronously on the
  *    caller's HIP stream (`stream` is a hipStream_t; NULL means the null stream);
  *    outputs are valid once that stream reaches the enqueued work.
  *  * Validation runs on the host before anything is enqueued: a non-FA_OK return
@@ -215,6 +218,28 @@ typedef struct fa_decode_args {
 size_t fa_decode_workspace_bytes(const fa_decode_args *args);
 fa_status fa_decode(const fa_decode_args *args, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Decode that allocates nothing: fa_decode with its workspace taken from a static
+ * device array of FA_DECODE_NOALLOC_MAX_WORKSPACE_BYTES bytes that the library holds on
+ * each GPU it runs on until the process ends.
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The call itself allocates and frees
+ * nothing (no hipMalloc, hipFree or allocating library routine); the caller passes the
+ * inputs and outputs exactly as for fa_decode.
+ *   args  as for fa_decode.
+ * Returns FA_ERR_WORKSPACE, launching nothing, when fa_decode_workspace_bytes(args)
+ * exceeds FA_DECODE_NOALLOC_MAX_WORKSPACE_BYTES (32 MiB: e.g. 64 sequences x 32 query
+ * heads x 16 chunks at D = 128 need 16.9 MB), and FA_ERR_DEVICE when no device is
+ * current.  The first call on a device looks up that device's array address (once per
+ * device, with the device current) and keeps it.
+ * Every call on one GPU shares that GPU's array, which keeps the previous call's
+ * partials; nothing in it needs clearing, since the merge reads only partials the same
+ * call's split kernel wrote.  Calls that overlap on one GPU (other streams, other host
+ * threads) race on the array: the caller must order them.
+ * ------------------------------------------------------------------------------- */
+#define FA_DECODE_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)32 << 20)
+fa_status fa_decode_noalloc(const fa_decode_args *args, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Forward and backward with dropout on P (bf16, D in {64, 128}).

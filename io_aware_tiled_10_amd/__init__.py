@@ -6,8 +6,9 @@ Python-side this package only marshals arguments (``binding``) and draws seeded
 synthetic inputs (``inputs``).
 """
 
-from .binding import (FaError, bwd, bwd_dropout, decode, decode_paged, device_supported,  # noqa: F401
+from .binding import (FaError, bwd, bwd_dropout, decode, decode_noalloc, decode_paged,  # noqa: F401
+                      device_supported,
                       fwd, fwd_dropout, fwd_fp8, fwd_varlen, lib, quantize_fp8)
 
-__all__ = ["fwd", "fwd_dropout", "fwd_varlen", "fwd_fp8", "quantize_fp8", "bwd", "bwd_dropout", "decode",
+__all__ = ["fwd", "fwd_dropout", "fwd_varlen", "fwd_fp8", "quantize_fp8", "bwd", "bwd_dropout", "decode", "decode_noalloc",
            "decode_paged", "device_supported", "lib", "FaError"]

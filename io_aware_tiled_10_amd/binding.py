@@ -114,7 +114,8 @@ class FwdFp8Args(ctypes.Structure):
 
 EXPORTED = ["fa_fwd", "fa_fwd_dropout", "fa_fwd_varlen", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd",
             "fa_bwd_dropout", "fa_bwd_workspace_bytes",
-            "fa_decode", "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
+            "fa_decode", "fa_decode_workspace_bytes", "fa_decode_noalloc",
+            "fa_decode_paged", "fa_decode_paged_workspace_bytes",
             "fa_status_str", "fa_device_supported", "fa_version"]
 
 _lib = None
@@ -137,6 +138,8 @@ def _open(path: str) -> ctypes.CDLL:
     h.fa_decode.restype = ctypes.c_int
     h.fa_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
     h.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+    h.fa_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+    h.fa_decode_noalloc.restype = ctypes.c_int
     h.fa_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs), ctypes.c_void_p]
     h.fa_fwd_varlen.restype = ctypes.c_int
     h.fa_decode_paged.argtypes = [ctypes.POINTER(DecodePagedArgs), ctypes.c_void_p,
@@ -566,6 +569,25 @@ def decode(q, k_cache, v_cache, seq_lens, max_len: Optional[int] = None, split_l
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib().fa_decode(ctypes.byref(a), _ptr(workspace), _workspace_bytes(workspace, q), _stream(q.device)))
     return o, lse
+
+
+# largest workspace fa_decode_noalloc takes from its static per-device array
+DECODE_NOALLOC_MAX_WORKSPACE_BYTES = 32 << 20
+
+
+def decode_noalloc(q, k_cache, v_cache, seq_lens, out: torch.Tensor, lse_out: Optional[torch.Tensor] = None,
+                   max_len: Optional[int] = None, split_len: int = 2048, scale: Optional[float] = None):
+    """Split-KV decode via ``fa_decode_noalloc``: the library takes the chunk partials
+    from its static per-device array, so this call allocates nothing (the caller passes
+    ``out`` and, if wanted, ``lse_out``).  Calls that overlap on one GPU race."""
+    _check_decode_inputs(q, k_cache, v_cache, seq_lens)
+    if max_len is None:
+        max_len = k_cache.shape[2]
+    _check_decode_outputs(q, out, lse_out)
+    _on_gpu(q)
+    a = decode_args(q, k_cache, v_cache, seq_lens, out, lse_out, max_len, split_len, scale)
+    _check(lib().fa_decode_noalloc(ctypes.byref(a), _stream(q.device)))
+    return out, lse_out
 
 
 def _check_decode_inputs(q, k_cache, v_cache, seq_lens) -> None:

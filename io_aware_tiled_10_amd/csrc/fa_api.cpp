@@ -10,6 +10,9 @@
 #include "fa.h"
 #include "fa_internal.h"
 
+static_assert(fa::kDecodeScratchBytes == FA_DECODE_NOALLOC_MAX_WORKSPACE_BYTES,
+              "the header states the decode scratch size");
+
 namespace fa {
 
 // Backward workspace: per query row the fp32 pair (LSE * log2 e, D_i).
@@ -430,12 +433,12 @@ size_t fa_decode_workspace_bytes(const fa_decode_args* a) {
   return fa::decode_workspace_bytes(a->Bs, a->Hq, decode_nsplit(a), a->D);
 }
 
-fa_status fa_decode(const fa_decode_args* a, void* workspace, size_t ws_bytes, void* stream) {
-  const fa_status st = validate_decode(a);
-  if (st != FA_OK || a->Bs == 0) return st;
+namespace {
+
+// The decode launch of fa_decode and fa_decode_noalloc: `a` is valid, Bs > 0, and
+// `workspace` holds at least decode_workspace_bytes() bytes.
+fa_status decode_launch(const fa_decode_args* a, void* workspace, void* stream) {
   const int nsplit = decode_nsplit(a);
-  const size_t need = fa::decode_workspace_bytes(a->Bs, a->Hq, nsplit, a->D);
-  if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return FA_ERR_WORKSPACE;
   fa::DecParams p{};
   p.q = static_cast<const uint16_t*>(a->q);
   p.k = static_cast<const uint16_t*>(a->k_cache);
@@ -458,6 +461,27 @@ fa_status fa_decode(const fa_decode_args* a, void* workspace, size_t ws_bytes, v
   p.scale_log2 = a->scale * 1.4426950408889634f;
   return map_launch_error(
       fa::launch_decode(p, a->D, a->out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+fa_status fa_decode(const fa_decode_args* a, void* workspace, size_t ws_bytes, void* stream) {
+  const fa_status st = validate_decode(a);
+  if (st != FA_OK || a->Bs == 0) return st;
+  const size_t need = fa::decode_workspace_bytes(a->Bs, a->Hq, decode_nsplit(a), a->D);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return FA_ERR_WORKSPACE;
+  return decode_launch(a, workspace, stream);
+}
+
+fa_status fa_decode_noalloc(const fa_decode_args* a, void* stream) {
+  const fa_status st = validate_decode(a);
+  if (st != FA_OK || a->Bs == 0) return st;
+  const size_t need = fa::decode_workspace_bytes(a->Bs, a->Hq, decode_nsplit(a), a->D);
+  if (need > fa::kDecodeScratchBytes) return FA_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  const hipError_t e = fa::decode_scratch(&scratch);
+  if (e != hipSuccess) return FA_ERR_DEVICE;  // no current device, or its array has no address
+  return decode_launch(a, scratch, stream);
 }
 
 fa_status fa_quantize_fp8(const fa_quantize_fp8_args* a, void* stream) {

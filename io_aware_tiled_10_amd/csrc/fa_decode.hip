@@ -27,10 +27,41 @@
 //  * a paged cache (interview answer, 高频追问 2: the blocked decode reads the paged KV
 //    blocks where they lie) changes only the descriptors: each 32-key block takes its
 //    page from the block table and the DMA reads the rows straight out of that page.
+#include <mutex>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
 namespace fa {
+
+// Partials of the decode entry point that allocates nothing (fa_decode_noalloc): one
+// array per GPU, held by the library until the process ends.  Host code never passes
+// `scratch` itself to a kernel (on the host it only names the symbol): each device's
+// address comes from hipGetSymbolAddress, below.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {  // first call on this device, which is current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u)) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 namespace {
 

@@ -95,4 +95,9 @@ struct DecParams {
 size_t decode_workspace_bytes(int Bs, int Hq, int nsplit, int D);
 hipError_t launch_decode(const DecParams& p, int D, int out_dtype, hipStream_t stream);
 
+// The static per-device array that fa_decode_noalloc uses as its workspace, and its
+// address on the current device (looked up once per device, then cached).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace fa

@@ -20,5 +20,6 @@ hipError_t launch_fwd_fp8(const FwdParams&, int, hipStream_t) { reached("launch_
 hipError_t launch_quantize_fp8(const QuantParams&, int, hipStream_t) { reached("launch_quantize_fp8"); }
 hipError_t launch_bwd(const BwdParams&, int, hipStream_t) { reached("launch_bwd"); }
 hipError_t launch_decode(const DecParams&, int, int, hipStream_t) { reached("launch_decode"); }
+hipError_t decode_scratch(void**) { reached("decode_scratch"); }
 
 }  // namespace fa

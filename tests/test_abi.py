@@ -160,6 +160,23 @@ def test_decode_workspace_query():
     assert fb.lib().fa_decode(ctypes.byref(good_dec(Bs=0)), None, 0, None) == OK
 
 
+@pytest.mark.parametrize("change,status", DEC_BAD)
+def test_decode_noalloc_rejects_bad_arguments(change, status):
+    # the same validation as fa_decode, before the static array is looked up
+    assert fb.lib().fa_decode_noalloc(ctypes.byref(good_dec(**change)), None) == status
+
+
+def test_decode_noalloc_rejects_work_beyond_its_static_array():
+    # 64 sequences x 32 heads x 16 chunks of partials fit the 32 MiB array; 33 chunks
+    # (a longer cache) need more and are refused before anything is looked up or launched
+    fits = good_dec(Bs=64, max_len=32768, cache_len=32768, split_len=2048)
+    assert fb.lib().fa_decode_workspace_bytes(ctypes.byref(fits)) <= fb.DECODE_NOALLOC_MAX_WORKSPACE_BYTES
+    big = good_dec(Bs=64, max_len=33 * 2048, cache_len=33 * 2048, split_len=2048)
+    assert fb.lib().fa_decode_workspace_bytes(ctypes.byref(big)) > fb.DECODE_NOALLOC_MAX_WORKSPACE_BYTES
+    assert fb.lib().fa_decode_noalloc(ctypes.byref(big), None) == WS
+    assert fb.lib().fa_decode_noalloc(ctypes.byref(good_dec(Bs=0)), None) == OK
+
+
 def good_varlen(**kw):
     a = fb.FwdVarlenArgs(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu_seqlens_q=FAKE, cu_seqlens_k=FAKE,
                          q_stride=fb.c_i64x2(4 * 128, 128), k_stride=fb.c_i64x2(2 * 128, 128),
@@ -298,3 +315,8 @@ def test_row_pitches_beyond_8_mib_are_rejected():
     assert fb.lib().fa_decode(ctypes.byref(good_dec(v_stride=fb.c_i64x3(0, 0, big))), FAKE, 1 << 30, None) == SHAPE
     assert fb.lib().fa_fwd_varlen(ctypes.byref(good_varlen(q_stride=fb.c_i64x2(big, 128))), None) == SHAPE
     assert fb.lib().fa_quantize_fp8(ctypes.byref(good_quant(x_stride=fb.c_i64x3(0, 0, big))), None) == SHAPE
+
+
+def test_noalloc_limit_matches_the_header():
+    m = re.search(r"#define FA_DECODE_NOALLOC_MAX_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == fb.DECODE_NOALLOC_MAX_WORKSPACE_BYTES
