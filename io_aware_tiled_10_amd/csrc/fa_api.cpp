@@ -15,15 +15,19 @@ static_assert(fa::kDecodeScratchBytes == FA_DECODE_NOALLOC_MAX_WORKSPACE_BYTES,
 
 namespace fa {
 
-// Backward workspace: per query row the fp32 pair (LSE * log2 e, D_i).
+// Backward workspace: two fp32 planes over the query rows, LSE * log2 e and then -D_i,
+// each rounded up to 256 bytes.
+static size_t bwd_plane_bytes(int B, int Hq, int Nq) { return ((size_t)B * Hq * Nq * 4 + 255) & ~size_t(255); }
+
 size_t bwd_workspace_bytes(int B, int Hq, int Nq, int D) {
   (void)D;
-  return ((size_t)B * Hq * Nq * 8 + 255) & ~size_t(255);
+  return 2 * bwd_plane_bytes(B, Hq, Nq);
 }
 
 void bwd_bind_workspace(BwdParams& p, void* workspace, int D) {
   (void)D;
-  p.stats = static_cast<float*>(workspace);
+  p.lse2 = static_cast<float*>(workspace);
+  p.negd = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_plane_bytes(p.B, p.Hq, p.Nq));
 }
 
 // Decode workspace: partial O [Bs, Hq, nsplit, D] fp32, then partial LSE [Bs, Hq, nsplit]

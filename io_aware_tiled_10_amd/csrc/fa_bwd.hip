@@ -10,8 +10,8 @@
 //
 // gfx950 mapping (three kernels in stream order, no atomics: every output element is
 // written once, so the backward is deterministic):
-//  1. bwd_pre: per query row, D_i = rowsum(dO * O) in fp32 and LSE * log2(e), stored
-//     side by side;
+//  1. bwd_pre: per query row, LSE * log2(e) and -D_i = -rowsum(dO * O) in fp32, in two
+//     planes;
 //  2. bwd_kv: one workgroup (8 waves) per 128-key tile of a KV head, walking the 64-row
 //     query tiles of every query head of the GQA group that can see the tile (causal:
 //     from the diagonal down).  Q, dO and the row statistics of each tile stream from
@@ -59,8 +59,8 @@ constexpr bool swz_period_ok() {
 }
 
 
-// Per query row: stats = (LSE * log2 e, D_i = sum_d dO_id O_id).  Rows whose LSE is -inf
-// (no visible key) get +inf, so their P is exactly zero.
+// Per query row: LSE * log2 e and -D_i = -sum_d dO_id O_id, in two planes.  Rows whose
+// LSE is -inf (no visible key) get +inf, so their P is exactly zero.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
   constexpr int TPR = D / 8;            // threads per row
@@ -83,9 +83,8 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
   for (int off = TPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, TPR);
   if (row < nrows && tid % TPR == 0) {
     const float L = p.lse[row];
-    const float l2 = L == -INFINITY ? INFINITY : L * kLog2e;
-    typedef float f32x2_t __attribute__((ext_vector_type(2)));
-    reinterpret_cast<f32x2_t*>(p.stats)[row] = f32x2_t{l2, sum};
+    p.lse2[row] = L == -INFINITY ? INFINITY : L * kLog2e;
+    p.negd[row] = -sum;
   }
 }
 
@@ -221,21 +220,22 @@ bwd_kv_kernel(BwdParams p) {
       rows = p.Nq - q0;
     }
     const int hq = hkv * p.G + gi;
-    if (wave == 0) {  // (lse2, D_i) of the tile's 64 rows, 512 bytes
-      const float* st = p.stats + 2 * (((int64_t)b * p.Hq + hq) * p.Nq + q0);
-      const auto rs = make_rsrc(st, rows <= 0 ? 0u : (uint32_t)(min(rows, BR) * 8));
-      lds_dma16(rs, dst + T::STATS, 16 * lane);
+    if (wave < 2) {  // LSE * log2 e (wave 0) or -D_i (wave 1) of the tile's 64 rows
+      const float* st = (wave == 0 ? p.lse2 : p.negd) + ((int64_t)b * p.Hq + hq) * p.Nq + q0;
+      const auto rs = make_rsrc(st, rows <= 0 ? 0u : (uint32_t)(min(rows, BR) * 4));
+      lds_dma4(rs, dst + T::STATS + 256 * wave, 4 * lane);
     }
     dma_rows(p.q + b * p.qs0 + hq * p.qs1 + (int64_t)q0 * p.qs2, p.qs2, BR, rows, dst, T::NDMA);
     dma_rows(p.dout + b * p.dos0 + hq * p.dos1 + (int64_t)q0 * p.dos2, p.dos2, BR, rows,
              dst + T::QBYTES, T::NDMA);
   };
-  // the previous tile's loads must have landed: all but this wave's latest group
+  // the previous tile's loads must have landed: all but this wave's latest group (waves
+  // 0 and 1 issue one statistics load more per tile)
   auto wait_ring = [&]() {
     if constexpr (T::NDMA == 2) {
-      if (wave == 0) FA_WAIT_VMCNT(5); else FA_WAIT_VMCNT(4);
+      if (wave < 2) FA_WAIT_VMCNT(5); else FA_WAIT_VMCNT(4);
     } else {
-      if (wave == 0) FA_WAIT_VMCNT(3); else FA_WAIT_VMCNT(2);
+      if (wave < 2) FA_WAIT_VMCNT(3); else FA_WAIT_VMCNT(2);
     }
   };
   static_assert(T::NDMA == 2 || T::NDMA == 1, "ring waits assume D = 128 or 64");
@@ -258,21 +258,41 @@ bwd_kv_kernel(BwdParams p) {
   unsigned char* px = lds + T::PX + kg * T::PXG + 16 * lane;  // + 1024 per 4 registers
   unsigned char* zt = lds + T::LDS_BYTES + kg * 32 * BR;
 
+  u32x4_t pkv[2][2];  // the dV role's P^T, kept from one step to the next without dropout
+
   // One query tile `it` in ring slot `slot` (uniform over the wave); `pboff` selects the
-  // P buffer of the key group's pair.
-  auto tile = [&](int it, int slot, uint32_t pboff) __attribute__((always_inline)) {
+  // P buffer of the key group's pair.  `first`: the first product and the role's
+  // elementwise work, leaving pk, the P^T (dV role) or dS^T (dK role) A operands of the
+  // second product; `second`: the second product, from pk.
+  auto tile = [&](int it, int slot, uint32_t pboff, bool first, bool second,
+                  u32x4_t (&pk)[2][2]) __attribute__((always_inline)) {
     const int qt = nqt - 1 - it / p.G;
     const int q0 = qt * BR;
     const unsigned char* qs = ring + slot * T::SLOT;
-    const float* st = reinterpret_cast<const float*>(qs + T::STATS);
+    const float* stl = reinterpret_cast<const float*>(qs + T::STATS);        // LSE * log2 e
+    const float* std_ = reinterpret_cast<const float*>(qs + T::STATS + 256);  // -D_i
+    // 4 consecutive rows 32 qb + 8 rg + 4 hi .. of a statistics plane
+    auto rows4 = [&](const float* plane, int qb, int rg) {
+      return *reinterpret_cast<const f32x4_t*>(plane + 32 * qb + 8 * rg + 4 * hi);
+    };
 
     // (1) S = Q K^T (dV role) or dP = dO V^T (dK role); rows = queries 32 qb + (register),
-    //     column = key
+    //     column = key.  Without dropout the dK role starts its products from -D_i, so they
+    //     leave dP - D_i, the factor of dS.
+    if (first) {
     const unsigned char* arows = qs + (dv_role ? 0 : T::QBYTES);
     f32x16_t sp[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       sp[qb] = f32x16_t{};
+      if (!DROP && !dv_role) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const f32x4_t nd = rows4(std_, qb, rg);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sp[qb][4 * rg + e] = nd[e];
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
         const int o = (32 * qb + l32) * T::ROWB + 16 * ((2 * ks + hi) ^ qsw);
@@ -280,7 +300,6 @@ bwd_kv_kernel(BwdParams p) {
       }
     }
 
-    u32x4_t pk[2][2];  // P^T (dV role) or dS^T (dK role) as A operands
     // dropout: the mask of the group's 32 keys and the tile's 64 queries, drawn as the
     // forward draws it (lane L: the words of query q0 + L) and spread into the group's
     // [key][query] byte table; each role draws one of the two 16-key halves
@@ -310,9 +329,7 @@ bwd_kv_kernel(BwdParams p) {
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
             const int ql = 32 * qb + 8 * rg + 4 * hi;
-            const f32x4_t st01 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql);
-            const f32x4_t st23 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql + 4);
-            const float l2[4] = {st01[0], st01[2], st23[0], st23[2]};
+            const f32x4_t l2 = rows4(stl, qb, rg);
             f32x4_t pv4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -372,10 +389,8 @@ bwd_kv_kernel(BwdParams p) {
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const int ql = 32 * qb + 8 * rg + 4 * hi;
-          const f32x4_t st01 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql);
-          const f32x4_t st23 = *reinterpret_cast<const f32x4_t*>(st + 2 * ql + 4);
-          const float dd[4] = {st01[1], st01[3], st23[1], st23[3]};
+          f32x4_t nd{};
+          if constexpr (DROP) nd = rows4(std_, qb, rg);
           f32x4_t pv4;
           if constexpr (DROP) {
             pv4 = *reinterpret_cast<const f32x4_t*>(px + 1024 * (4 * qb + rg));
@@ -388,9 +403,9 @@ bwd_kv_kernel(BwdParams p) {
           if constexpr (DROP) zw = mask_word(qb, rg);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float dpz = sp[qb][4 * rg + e];
-            if constexpr (DROP) dpz = dropout_keep(zw, e, p.drop_t) ? dpz * p.drop_scale : 0.f;
-            sp[qb][4 * rg + e] = pv4[e] * (dpz - dd[e]);
+            float dpz = sp[qb][4 * rg + e];  // dP - D_i, or dP with dropout
+            if constexpr (DROP) dpz = (dropout_keep(zw, e, p.drop_t) ? dpz * p.drop_scale : 0.f) + nd[e];
+            sp[qb][4 * rg + e] = pv4[e] * dpz;
           }
         }
 #pragma unroll
@@ -402,33 +417,42 @@ bwd_kv_kernel(BwdParams p) {
             pk[qb][h2][w] = pack_bf16(sp[qb][8 * h2 + 2 * w], sp[qb][8 * h2 + 2 * w + 1]);
     }
 
+    }  // first
+
     // (2) acc += pk x (dO rows for the dV role, Q rows for the dK role), k-step ts = 2 qb
     //     + h2 holding queries 16 ts + 8 (e/4) + 4 hi + e%4, which the transposing reads
-    //     reproduce
-#pragma unroll
-    for (int d0 = 0; d0 < T::DB; d0 += 2) {
+    //     reproduce.  The 8 reads of 32-column block d + 1 are issued before the products
+    //     of block d (LDS returns in order: with block d + 1's reads outstanding, a count
+    //     of 8 means block d has arrived).
+    if (second) {
       u32x2_t f[2][4][2];
       constexpr int TS = 16 * T::ROWB, SO = 0;
-#pragma unroll
-      for (int dd = 0; dd < 2; ++dd)
+      const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(slot * T::SLOT);
+      auto tread = [&](int d, u32x2_t (&w)[4][2]) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-          const uint32_t a = trb[r][d0 + dd] + (uint32_t)__builtin_amdgcn_readfirstlane(slot * T::SLOT);
-          lds_read_tr16x2<SO, SO + TS>(f[dd][0][r], f[dd][1][r], a);
-          lds_read_tr16x2<SO + 2 * TS, SO + 3 * TS>(f[dd][2][r], f[dd][3][r], a);
+          const uint32_t a = trb[r][d] + soff;
+          lds_read_tr16x2<SO, SO + TS>(w[0][r], w[1][r], a);
+          lds_read_tr16x2<SO + 2 * TS, SO + 3 * TS>(w[2][r], w[3][r], a);
+        }
+      };
+      tread(0, f[0]);
+#pragma unroll
+      for (int d = 0; d < T::DB; ++d) {
+        u32x2_t (&w)[4][2] = f[d & 1];
+        if (d + 1 < T::DB) {
+          tread(d + 1, f[(d + 1) & 1]);
+          lds_wait_tr<8>(w[0][0], w[0][1], w[1][0], w[1][1]);
+          lds_wait_tr<8>(w[2][0], w[2][1], w[3][0], w[3][1]);
+        } else {
+          lds_wait_tr(w[0][0], w[0][1], w[1][0], w[1][1]);
+          lds_wait_tr(w[2][0], w[2][1], w[3][0], w[3][1]);
         }
 #pragma unroll
-      for (int dd = 0; dd < 2; ++dd) {
-        lds_wait_tr(f[dd][0][0], f[dd][0][1], f[dd][1][0], f[dd][1][1]);
-        lds_wait_tr(f[dd][2][0], f[dd][2][1], f[dd][3][0], f[dd][3][1]);
-      }
-#pragma unroll
-      for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
         for (int ts = 0; ts < 4; ++ts)
-          acc[d0 + dd] = mfma32(pk[ts >> 1][ts & 1],
-                                u32x4_t{f[dd][ts][0][0], f[dd][ts][0][1], f[dd][ts][1][0], f[dd][ts][1][1]},
-                                acc[d0 + dd]);
+          acc[d] = mfma32(pk[ts >> 1][ts & 1],
+                          u32x4_t{w[ts][0][0], w[ts][0][1], w[ts][1][0], w[ts][1][1]}, acc[d]);
+      }
     }
 
   };
@@ -439,13 +463,25 @@ bwd_kv_kernel(BwdParams p) {
   // (dK role), s (dV role) and s + 1 (loading) are in use, and iters + 1 steps run.  With
   // dropout both roles take tile s in step s (their barrier inside the tile publishes the
   // mask table) and the ring loads two tiles ahead.  Every wave passes the same barriers.
+  // Without dropout the dV role also turns its work around: in step s it first adds
+  // P(s - 1)^T dO(s - 1) (P kept in registers from step s - 1, dO still in slot s - 1), then
+  // forms S and P of tile s.  Its exps then run beside the dK role's second product and
+  // the dK role's dS work beside the dV role's products, instead of both roles' elementwise
+  // work falling together between their products.
   constexpr int AHEAD = DROP ? 2 : 1, LAG = DROP ? 0 : 1;
-  auto step = [&](int st, auto slot_c) __attribute__((always_inline)) {
+  auto step = [&](int st, auto slot_c, auto role) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
+    constexpr bool DV = decltype(role)::value;  // == dv_role
     issue(st + AHEAD, (slot + AHEAD) % NS);
-    const int lag = dv_role ? 0 : LAG;
-    const int it = st - lag;
-    if (it >= 0 && it < iters) tile(it, (slot + NS - lag) % NS, (uint32_t)(it & 1) * 4096u);
+    if (!DROP && DV) {
+      if (st >= 1 && st - 1 < iters) tile(st - 1, (slot + NS - 1) % NS, 0u, false, true, pkv);
+      if (st < iters) tile(st, slot, (uint32_t)(st & 1) * 4096u, true, false, pkv);
+    } else {
+      const int lag = DV ? 0 : LAG;
+      const int it = st - lag;
+      u32x4_t pk[2][2];
+      if (it >= 0 && it < iters) tile(it, (slot + NS - lag) % NS, (uint32_t)(it & 1) * 4096u, true, true, pk);
+    }
     if constexpr (DROP) wait_ring();  // tile st + 1 has landed (only st + 2 may be in flight)
     else FA_WAIT_VMCNT(0);            // tile st + 1 has landed
     FA_WAIT_LGKMCNT0();               // this wave's ring and P accesses are done
@@ -460,14 +496,23 @@ bwd_kv_kernel(BwdParams p) {
     FA_WAIT_LGKMCNT0();
     FA_BARRIER();
     const int nsteps = iters + LAG;
-    int st = 0;
-    for (; st + 2 < nsteps; st += 3) {
-      step(st, std::integral_constant<int, 0>{});
-      step(st + 1, std::integral_constant<int, 1>{});
-      step(st + 2, std::integral_constant<int, 2>{});
-    }
-    if (st < nsteps) step(st, std::integral_constant<int, 0>{});
-    if (st + 1 < nsteps) step(st + 1, std::integral_constant<int, 1>{});
+    // without dropout one loop per role (each with its own register allocation: the dV
+    // role keeps its P from one step to the next); both pass the same barriers.  With
+    // dropout the roles' steps do not depend on the role at compile time: one loop.
+    auto run = [&](auto role) __attribute__((always_inline)) {
+      int st = 0;
+      for (; st + 2 < nsteps; st += 3) {
+        step(st, std::integral_constant<int, 0>{}, role);
+        step(st + 1, std::integral_constant<int, 1>{}, role);
+        step(st + 2, std::integral_constant<int, 2>{}, role);
+      }
+      if (st < nsteps) step(st, std::integral_constant<int, 0>{}, role);
+      if (st + 1 < nsteps) step(st + 1, std::integral_constant<int, 1>{}, role);
+    };
+    if (!DROP && dv_role)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
   }
 
   // ---- dV = acc (dV role) or dK = scale * acc (dK role), rounded to bf16; rows >= Nk
@@ -573,10 +618,9 @@ bwd_q_kernel(BwdParams p) {
       df[s] = buf_load16(rd, od + 32 * s);
     }
     if (qi < p.Nq) {
-      typedef float f32x2_t __attribute__((ext_vector_type(2)));
-      const f32x2_t st = reinterpret_cast<const f32x2_t*>(p.stats)[((int64_t)b * p.Hq + hq) * p.Nq + qi];
-      l2 = st[0];
-      dd = st[1];
+      const int64_t row = ((int64_t)b * p.Hq + hq) * p.Nq + qi;
+      l2 = p.lse2[row];
+      dd = -p.negd[row];
     } else {
       l2 = INFINITY;  // padding rows: P = 0
     }

@@ -139,6 +139,11 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, u
                                              (int)off, soff, 0, 0);
 }
 
+// The same with 4 bytes per lane: lane t's dword lands at lds + 4 t (256 bytes per wave).
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, (int)off, 0, 0, 0);
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding; also a
 // compiler barrier for memory accesses.
 //

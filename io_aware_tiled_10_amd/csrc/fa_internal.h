@@ -57,7 +57,8 @@ struct BwdParams {
   const float* lse;
   uint16_t *dq, *dk, *dv;
   const int32_t* kv_lens;
-  float* stats;   // [B, Hq, Nq] x (LSE * log2 e, D_i) workspace
+  float* lse2;    // [B, Hq, Nq] workspace: LSE * log2 e of each query row (+inf if LSE = -inf)
+  float* negd;    // [B, Hq, Nq] workspace: -D_i = -sum_d dO_id O_id of each query row
   int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2, dos0, dos1, dos2;
   int64_t dqs0, dqs1, dqs2, dks0, dks1, dks2, dvs0, dvs1, dvs2;
   int B, Hq, Hkv, Nq, Nk, G, nkt;
@@ -68,7 +69,8 @@ struct BwdParams {
 };
 
 size_t bwd_workspace_bytes(int B, int Hq, int Nq, int D);
-// Points p.stats into a workspace of bwd_workspace_bytes() bytes.
+// Points p.lse2 and p.negd into a workspace of bwd_workspace_bytes() bytes (p.B, p.Hq
+// and p.Nq set).
 void bwd_bind_workspace(BwdParams& p, void* workspace, int D);
 hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t stream);
 

@@ -120,7 +120,7 @@ def test_bwd_workspace_query_and_too_small_workspace():
     a = good_bwd(B=2, Hq=16, Hkv=16, Nq=4096, Nk=4096)
     need = fb.lib().fa_bwd_workspace_bytes(ctypes.byref(a))
     rows = 2 * 16 * 4096
-    assert need == rows * 8  # (LSE log2 e, D_i) per query row, fp32
+    assert need == rows * 8  # LSE log2 e and -D_i per query row, two fp32 planes
     assert fb.lib().fa_bwd(ctypes.byref(a), FAKE, need - 1, None) == WS
     assert fb.lib().fa_bwd(ctypes.byref(a), None, need, None) == WS
     assert fb.lib().fa_bwd(ctypes.byref(a), FAKE + 4, need, None) == WS
