@@ -32,6 +32,7 @@
 //     accumulating dQ inside bwd_kv, but removes the device-scope fp32 atomics, which
 //     on a multi-XCD part are executed beyond the per-XCD L2.
 #include <type_traits>
+#include <utility>
 
 #include "fa_common.h"
 #include "fa_internal.h"
@@ -39,6 +40,17 @@
 namespace fa {
 
 namespace {
+
+// f(std::integral_constant<int, s>{}) for s = 0 .. N - 1, in order: a loop over ring
+// slots whose index is a compile-time constant in each call.
+template <typename F, int... S>
+__device__ __forceinline__ void for_each_slot_impl(F&& f, std::integer_sequence<int, S...>) {
+  (f(std::integral_constant<int, S>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void for_each_slot(F&& f) {
+  for_each_slot_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // 16-byte slot swizzle of row r of a staged tile with `rowb`-byte rows: 16 consecutive
 // rows read at one logical slot hit 16 different slots, and 8 consecutive rows read over
@@ -538,7 +550,7 @@ bwd_kv_kernel(BwdParams p) {
 // ------------------------------------------------------------------------------------
 constexpr int kDqBC = 64;             // keys per block
 
-template <int D, int NW, int NS>
+template <int D, int NW, int NS, bool ROT = false>
 struct DqTile {
   static constexpr int BR = 32 * NW;                         // query rows per workgroup
   static constexpr int KS = D / 16;
@@ -548,17 +560,23 @@ struct DqTile {
   static constexpr int RPI = 1024 / ROWB;
   static constexpr int TBYTES = kDqBC * ROWB;                // one K or V block
   static constexpr int NDMA = TBYTES / (1024 * NW);          // per thread per tensor
-  static constexpr int AHEAD = NS - 1;                       // blocks in flight
+  // blocks in flight; with the rotated order a slot stays in use one block longer
+  static constexpr int AHEAD = ROT ? NS - 2 : NS - 1;
+  static_assert(AHEAD >= 1, "at least one block must be in flight");
   static constexpr int LDS_BYTES = 2 * NS * TBYTES;
   static_assert(NDMA * 1024 * NW == TBYTES, "a block must split evenly over the waves");
   static __device__ __forceinline__ int swz(int r) { return swz_rows<ROWB>(r); }
 };
 
-// NW waves (32 query rows each) per workgroup; NS-slot ring (NS - 1 blocks ahead).
-template <int D, int NW, int NS, bool DROP = false>
+// NW waves (32 query rows each) per workgroup; NS-slot ring.  ROT: the second half of
+// the waves takes each block's work in the rotated order (dQ of the previous block first,
+// then S, dP and dS of this one), so the two waves of a SIMD run their elementwise work
+// beside each other's products.
+template <int D, int NW, int NS, bool DROP = false, bool ROT = false>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_q_kernel(BwdParams p) {
-  using T = DqTile<D, NW, NS>;
+  using T = DqTile<D, NW, NS, ROT>;
+  static_assert(!(ROT && DROP), "the rotated order is built for the path without dropout");
   constexpr int BR = T::BR, BC = kDqBC;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[T::LDS_BYTES];
   unsigned char* kring = lds;
@@ -626,6 +644,9 @@ bwd_q_kernel(BwdParams p) {
     }
     asm volatile("" ::: "memory");  // issue these before the ring loads below
   }
+  f32x16_t ndv;  // -D_i in every register: the start of each dP^T product without dropout
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndv[r] = -dd;
 
   const uint16_t* kbase = p.k + b * p.ks0 + hkv * p.ks1;
   const uint16_t* vbase = p.v + b * p.vs0 + hkv * p.vs1;
@@ -678,56 +699,47 @@ bwd_q_kernel(BwdParams p) {
       ktb[r][d] = kring_addr + row * T::ROWB + 16 * ((4 * d + vlo) ^ T::swz(row)) + 8 * (vi & 1);
     }
 
-  // One block; `slot_c` is j % NS as a compile-time constant.
-  auto block = [&](int j, auto slot_c) {
+  // S, dP and dS of block j (slot `slot_c`, j % NS as a compile-time constant) into pf.
+  auto sdp = [&](int j, auto slot_c, u32x4_t (&pf)[4]) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
-    dma(j + T::AHEAD, (slot + T::AHEAD) % NS);  // into the slot block j - 1 finished with
     const unsigned char* ks = kring + slot * T::TBYTES;
     const unsigned char* vs = vring + slot * T::TBYTES;
 
-    // S^T = K Q^T and dP^T = V dO^T for keys [0, 32) and [32, 64) of the block
-    f32x16_t s[2], dp[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) s[h] = dp[h] = f32x16_t{};
-#pragma unroll
-    for (int k = 0; k < T::KS; ++k) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int o = (32 * h + l32) * T::ROWB + 16 * ((2 * k + hi) ^ rsw);
-        const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(ks + o);
-        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(vs + o);
-        s[h] = mfma32(ak, qf[k], s[h]);
-        dp[h] = mfma32(av, df[k], dp[h]);
-      }
-    }
-
-    // P^T = exp(S^T - LSE), dS^T = P^T (dP^T - D_i), zero where the pair does not exist;
-    // packed as the B operand of dQ^T += K^T dS^T (k-step ts: keys 16 ts + 8 (e/4) +
-    // 4 hi + e%4, e = 0..7)
+    // Each 32-key half h of the block in turn: S^T = K Q^T and dP^T = V dO^T for keys
+    // 32 h .. 32 h + 31 (without dropout dP^T starts from -D_i, so the products leave
+    // dP^T - D_i), then P^T = exp(S^T - LSE) and dS^T = P^T (dP^T - D_i), zero where the
+    // pair does not exist, packed as the B operand of dQ^T += K^T dS^T (k-step ts: keys
+    // 16 ts + 8 (e/4) + 4 hi + e%4, e = 0..7).  The first half's elementwise work can run
+    // beside the second half's products.
     const int key0 = j * BC;
     const bool edge = (key0 + BC > lk) || (p.causal && key0 + BC - 1 > q_wg0 + diag);
     const int last = p.causal ? min(lk - 1, qi + diag) : lk - 1;
-    u32x4_t pf[4];
-    // dropout: the forward's mask words of this lane's query for the block's two halves
-    u32x4_t zw[2] = {};
-    if constexpr (DROP) {
-      zw[0] = dropout_words(key0 / 32, hi, qi, hq, b, p.seed_lo, p.seed_hi);
-      zw[1] = dropout_words(key0 / 32 + 1, hi, qi, hq, b, p.seed_lo, p.seed_hi);
-    }
-    auto grads = [&](auto masked) {  // two instances: blocks crossing no edge test nothing
-      constexpr bool M = decltype(masked)::value;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
+      f32x16_t sh{}, dph = DROP ? f32x16_t{} : ndv;
+#pragma unroll
+      for (int k = 0; k < T::KS; ++k) {
+        const int o = (32 * h + l32) * T::ROWB + 16 * ((2 * k + hi) ^ rsw);
+        const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(ks + o);
+        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(vs + o);
+        sh = mfma32(ak, qf[k], sh);
+        dph = mfma32(av, df[k], dph);
+      }
+      // dropout: the forward's mask words of this lane's query for this half
+      u32x4_t zw{};
+      if constexpr (DROP) zw = dropout_words(key0 / 32 + h, hi, qi, hq, b, p.seed_lo, p.seed_hi);
+      auto grads = [&](auto masked) {  // two instances: blocks crossing no edge test nothing
+        constexpr bool M = decltype(masked)::value;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           float v2[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const float pv = fast_exp2(fmaf(s[h][r + e], c, -l2));
-            float dpz = dp[h][r + e];
+            const float pv = fast_exp2(fmaf(sh[r + e], c, -l2));
+            float dpz = dph[r + e];  // dP - D_i, or dP with dropout
             if constexpr (DROP)
-              dpz = dropout_keep(zw[h][(r + e) >> 2], (r + e) & 3, p.drop_t) ? dpz * p.drop_scale : 0.f;
-            float ds = pv * (dpz - dd);
+              dpz = (dropout_keep(zw[(r + e) >> 2], (r + e) & 3, p.drop_t) ? dpz * p.drop_scale : 0.f) - dd;
+            float ds = pv * dpz;
             if constexpr (M) {
               const int key = key0 + 32 * h + 8 * ((r + e) >> 2) + 4 * hi + ((r + e) & 3);
               ds = key > last ? 0.f : ds;
@@ -736,44 +748,89 @@ bwd_q_kernel(BwdParams p) {
           }
           pf[2 * h + (r >> 3)][(r & 7) >> 1] = pack_bf16(v2[0], v2[1]);
         }
-    };
-    if (edge)
-      grads(std::true_type{});
-    else
-      grads(std::false_type{});
+      };
+      if (edge)
+        grads(std::true_type{});
+      else
+        grads(std::false_type{});
+    }
+  };
 
-    // dQ^T += K^T dS^T; K^T fragments from transposing reads of the K block
-#pragma unroll
-    for (int d = 0; d < T::DB; ++d) {
-      u32x2_t kt[4][2];
+  // dQ^T += K^T dS^T for the block in slot `slot_c` with its dS^T in pf; K^T fragments
+  // from transposing reads of the K block, those of 32-column block d + 1 issued before
+  // the products of block d (LDS returns in order: with block d + 1's 8 reads
+  // outstanding, a count of 8 means block d has arrived)
+  auto dq = [&](auto slot_c, const u32x4_t (&pf)[4]) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
+    {
+      u32x2_t kt[2][4][2];
       constexpr int SO = slot * T::TBYTES, TS = 16 * T::ROWB;
+      auto kread = [&](int d, u32x2_t (&w)[4][2]) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        lds_read_tr16<SO>(kt[0][r], ktb[r][d]);
-        lds_read_tr16<SO + TS>(kt[1][r], ktb[r][d]);
-        lds_read_tr16<SO + 2 * TS>(kt[2][r], ktb[r][d]);
-        lds_read_tr16<SO + 3 * TS>(kt[3][r], ktb[r][d]);
+        for (int r = 0; r < 2; ++r) {
+          lds_read_tr16x2<SO, SO + TS>(w[0][r], w[1][r], ktb[r][d]);
+          lds_read_tr16x2<SO + 2 * TS, SO + 3 * TS>(w[2][r], w[3][r], ktb[r][d]);
+        }
+      };
+      kread(0, kt[0]);
+#pragma unroll
+      for (int d = 0; d < T::DB; ++d) {
+        u32x2_t (&w)[4][2] = kt[d & 1];
+        if (d + 1 < T::DB) {
+          kread(d + 1, kt[(d + 1) & 1]);
+          lds_wait_tr<8>(w[0][0], w[0][1], w[1][0], w[1][1]);
+          lds_wait_tr<8>(w[2][0], w[2][1], w[3][0], w[3][1]);
+        } else {
+          lds_wait_tr(w[0][0], w[0][1], w[1][0], w[1][1]);
+          lds_wait_tr(w[2][0], w[2][1], w[3][0], w[3][1]);
+        }
+#pragma unroll
+        for (int ts = 0; ts < 4; ++ts)
+          acc[d] = mfma32(u32x4_t{w[ts][0][0], w[ts][0][1], w[ts][1][0], w[ts][1][1]}, pf[ts], acc[d]);
       }
-      lds_wait_tr(kt[0][0], kt[0][1], kt[1][0], kt[1][1]);
-      lds_wait_tr(kt[2][0], kt[2][1], kt[3][0], kt[3][1]);
-#pragma unroll
-      for (int ts = 0; ts < 4; ++ts)
-        acc[d] = mfma32(u32x4_t{kt[ts][0][0], kt[ts][0][1], kt[ts][1][0], kt[ts][1][1]}, pf[ts], acc[d]);
     }
 
-    // block j + 1 has landed (only later blocks may be in flight); the barrier publishes
-    // it and frees this block's slot
-    wait_vmcnt<kInFlight>();
-    FA_WAIT_LGKMCNT0();
-    FA_BARRIER();
   };
-  static_assert(NS == 2, "the loop below walks two slots");
-  int j = 0;
-  for (; j + 1 < nblk; j += 2) {
-    block(j, std::integral_constant<int, 0>{});
-    block(j + 1, std::integral_constant<int, 1>{});
-  }
-  if (j < nblk) block(j, std::integral_constant<int, 0>{});
+
+  // One step j: load block j + AHEAD into the slot that is free, the block's work (the
+  // rotated order first finishes block j - 1 with its dQ), then the barrier: block j + 1
+  // has landed (only later blocks may be in flight), and the barrier publishes it and
+  // frees the slot read longest ago.  Every wave passes the same barriers.
+  auto run = [&](auto rot) __attribute__((always_inline)) {
+    constexpr bool R = decltype(rot)::value;
+    u32x4_t pf[4];
+    auto step = [&](int j, auto slot_c) __attribute__((always_inline)) {
+      constexpr int slot = decltype(slot_c)::value;
+      dma(j + T::AHEAD, (slot + T::AHEAD) % NS);
+      if constexpr (R) {
+        if (j >= 1) dq(std::integral_constant<int, (slot + NS - 1) % NS>{}, pf);
+        sdp(j, slot_c, pf);
+      } else {
+        sdp(j, slot_c, pf);
+        dq(slot_c, pf);
+      }
+      wait_vmcnt<kInFlight>();
+      FA_WAIT_LGKMCNT0();
+      FA_BARRIER();
+    };
+    int j = 0;
+    for (; j + NS - 1 < nblk; j += NS)
+      for_each_slot<NS>([&](auto sc) { step(j + decltype(sc)::value, sc); });
+    for_each_slot<NS - 1>([&](auto sc) {
+      if (j + decltype(sc)::value < nblk) step(j + decltype(sc)::value, sc);
+    });
+    FA_WAIT_VMCNT(0);  // the trailing loads (past the keys: zeros) write the ring too
+    if constexpr (R) {  // the last block's dQ, after the last barrier
+      const int sl = (nblk - 1) % NS;
+      for_each_slot<NS>([&](auto sc) {
+        if (sl == decltype(sc)::value) dq(sc, pf);
+      });
+    }
+  };
+  if (ROT && wave >= NW / 2)
+    run(std::bool_constant<ROT>{});
+  else
+    run(std::false_type{});
 
   // ---- dQ = scale * acc (lane = query row, register = head-dim element)
   if (qi < p.Nq) {
@@ -807,11 +864,18 @@ hipError_t launch_all(BwdParams p, hipStream_t stream) {
   p.nkt = (p.Nk + kKvBC - 1) / kKvBC;
   e = launch(bwd_kv_kernel<D, DROP>, (int64_t)p.nkt * p.Hkv * p.B, 64 * kKvWaves, p, stream);
   if (e != hipSuccess) return e;
-  // 128-row query tiles, two workgroups per compute unit: finer causal load balance than
-  // 256-row tiles at these grid sizes (measured 0.91 -> 0.80 ms for B2 H16 N4096 D128)
-  constexpr int NW = 4, NS = 2;
-  const int64_t nqt = (p.Nq + 32 * NW - 1) / (32 * NW);
-  return launch(bwd_q_kernel<D, NW, NS, DROP>, nqt * p.Hq * p.B, 64 * NW, p, stream);
+  // without dropout: 256-row query tiles of 8 waves, the second four in the rotated
+  // order, on a four-slot ring (two blocks ahead); with dropout: 128-row tiles of 4 waves,
+  // two workgroups per compute unit, on a two-slot ring
+  if constexpr (DROP) {
+    constexpr int NW = 4, NS = 2;
+    const int64_t nqt = (p.Nq + 32 * NW - 1) / (32 * NW);
+    return launch(bwd_q_kernel<D, NW, NS, true>, nqt * p.Hq * p.B, 64 * NW, p, stream);
+  } else {
+    constexpr int NW = 8, NS = 4;
+    const int64_t nqt = (p.Nq + 32 * NW - 1) / (32 * NW);
+    return launch(bwd_q_kernel<D, NW, NS, false, true>, nqt * p.Hq * p.B, 64 * NW, p, stream);
+  }
 }
 
 }  // namespace

@@ -433,6 +433,7 @@ fwd_bf16_kernel(FwdParams p) {
   if (j < nblk) step(j, Slot<1>{}, sb0, sb1, sa0, sa1, Later{});
   if (j + 1 < nblk) step(j + 1, Slot<2>{}, sa0, sa1, sb0, sb1, Later{});
   if (j + 2 < nblk) step(j + 2, Slot<3>{}, sb0, sb1, sa0, sa1, Later{});
+  FA_WAIT_VMCNT(0);  // the trailing loads (past the keys: zeros) write the ring too
 
   // ---- epilogue: O = acc / l once (times 1 / keep with dropout); LSE = m * scale + ln(l).
   // l == 0 only when no key was visible (O = 0, LSE = -inf); a NaN l (a NaN score) stays
