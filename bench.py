@@ -296,10 +296,17 @@ def _host_cpu():
     try:
         import subprocess
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        f = {}
         for ln in out.splitlines():
-            if ln.strip().startswith("Model name"):
-                model = ln.split(":", 1)[1].strip()
-                break
+            if ":" in ln:
+                k, v = ln.split(":", 1)
+                f.setdefault(k.strip(), v.strip())
+        model = f.get("Model name", "")
+        # a virtualised host may report only the vendor line: add the CPUID family, model
+        # and stepping, which name the part
+        ids = [f"{k.lower()} {f[k]}" for k in ("CPU family", "Model", "Stepping") if f.get(k)]
+        if model and ids:
+            model = f"{model} ({', '.join(ids)})"
     except Exception:  # pragma: no cover
         pass
     if not model:
