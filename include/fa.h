@@ -147,10 +147,11 @@ fa_status fa_fwd(const fa_fwd_args *args, void *stream);
  *   kv_lens, scale, causal as in the forward; rows of dk/dv at positions >= Lk are 0.
  * The workspace (device, caller-owned, at least fa_bwd_workspace_bytes() bytes, 16-byte
  * aligned, any contents) holds two fp32 planes [B, Hq, Nq], each padded to a multiple of
- * 256 bytes: LSE * log2 e, then -D_i = -rowsum(dO * O); it is written by the call itself.  Three kernels run in stream
- * order: the per-row statistics, dK/dV (one workgroup per key tile) and dQ (one
- * workgroup per query tile, recomputing S and dP).  No atomics are used: results are
- * bitwise reproducible run to run.
+ * 256 bytes: LSE * log2 e, then -D_i = -rowsum(dO * O); it is written by the call
+ * itself.  Two kernels run in stream order: dQ (one workgroup per query tile,
+ * recomputing S and dP; it also forms and stores the row statistics) and dK/dV (one
+ * workgroup per key tile).  No atomics are used: results are bitwise reproducible run
+ * to run.
  * ------------------------------------------------------------------------------- */
 typedef struct fa_bwd_args {
   const void *q, *k, *v, *o, *dout;

@@ -8,10 +8,19 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = rowsum(dO * O),  dS = P * (dP - D_i),
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// gfx950 mapping (three kernels in stream order, no atomics: every output element is
+// gfx950 mapping (two kernels in stream order, no atomics: every output element is
 // written once, so the backward is deterministic):
-//  1. bwd_pre: per query row, LSE * log2(e) and -D_i = -rowsum(dO * O) in fp32, in two
-//     planes;
+//  1. bwd_q: the forward's layout turned to dQ.  One workgroup (8 waves, 256 rows; with
+//     dropout 4 waves, 128 rows) per query tile, Q and dO rows resident as MFMA operands,
+//     K/V blocks of 64 keys through an LDS ring; per block S^T = K Q^T and dP^T = V dO^T
+//     (one lane per query), P^T = exp(S^T - LSE), dS^T = P^T (dP^T - D_i), and
+//     dQ^T += K^T dS^T with K^T from transposing reads; dQ = scale * acc, once.  Each
+//     lane first forms its row's statistics, LSE * log2(e) and -D_i = -rowsum(dO * O)
+//     in fp32, and stores them in two planes for the next kernel (the row's dO is
+//     loaded anyway; every row of every query tile is covered, whether or not it sees
+//     a key).  Recomputing S and dP here costs two more products per (query, key) pair
+//     than accumulating dQ inside bwd_kv, but removes the device-scope fp32 atomics,
+//     which on a multi-XCD part are executed beyond the per-XCD L2;
 //  2. bwd_kv: one workgroup (8 waves) per 128-key tile of a KV head, walking the 64-row
 //     query tiles of every query head of the GQA group that can see the tile (causal:
 //     from the diagonal down).  Q, dO and the row statistics of each tile stream from
@@ -22,15 +31,7 @@
 //     first, so it never waits for P inside a step (with dropout both take the same
 //     tile and meet at a barrier).  On
 //     32x32x16 bf16 MFMA with one lane per key, P and dS are already the A operands of
-//     the second products, whose dO^T and Q^T come from transposing LDS reads;
-//  3. bwd_q: the forward's layout turned to dQ.  One workgroup (4 waves) per 128-row
-//     query tile, two per compute unit, Q and dO rows resident as MFMA operands, K/V
-//     blocks of 64 keys through a two-slot LDS ring; per block S^T = K Q^T and dP^T = V dO^T (one lane
-//     per query), P^T = exp(S^T - LSE), dS^T = P^T (dP^T - D_i), and
-//     dQ^T += K^T dS^T with K^T from transposing reads; dQ = scale * acc, once.
-//     Recomputing S and dP here costs two more products per (query, key) pair than
-//     accumulating dQ inside bwd_kv, but removes the device-scope fp32 atomics, which
-//     on a multi-XCD part are executed beyond the per-XCD L2.
+//     the second products, whose dO^T and Q^T come from transposing LDS reads.
 #include <type_traits>
 #include <utility>
 
@@ -70,35 +71,6 @@ constexpr bool swz_period_ok() {
   return true;
 }
 
-
-// Per query row: LSE * log2 e and -D_i = -sum_d dO_id O_id, in two planes.  Rows whose
-// LSE is -inf (no visible key) get +inf, so their P is exactly zero.
-template <int D>
-__global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
-  constexpr int TPR = D / 8;            // threads per row
-  constexpr int RPB = 256 / TPR;        // rows per block
-  const int tid = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;  // over B * Hq * Nq
-  const int col = 8 * (tid % TPR);
-  const int64_t nrows = (int64_t)p.B * p.Hq * p.Nq;
-  float sum = 0.f;
-  if (row < nrows) {
-    const int i = (int)(row % p.Nq);
-    const int64_t bh = row / p.Nq;
-    const int hq = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-    const u32x4_t o = *reinterpret_cast<const u32x4_t*>(p.o + b * p.os0 + hq * p.os1 + (int64_t)i * p.os2 + col);
-    const u32x4_t g = *reinterpret_cast<const u32x4_t*>(p.dout + b * p.dos0 + hq * p.dos1 + (int64_t)i * p.dos2 + col);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) sum += bf16_lo(o[w]) * bf16_lo(g[w]) + bf16_hi(o[w]) * bf16_hi(g[w]);
-  }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, TPR);
-  if (row < nrows && tid % TPR == 0) {
-    const float L = p.lse[row];
-    p.lse2[row] = L == -INFINITY ? INFINITY : L * kLog2e;
-    p.negd[row] = -sum;
-  }
-}
 
 // ------------------------------------------------------------------------------------
 // dK/dV: key-tile outer loop, each 32-key group's work split between two waves.
@@ -611,38 +583,59 @@ bwd_q_kernel(BwdParams p) {
   const int nblk = (kend + BC - 1) / BC;
   const int qi = q_wg0 + wave * 32 + l32;  // this lane's query row
 
-  uint16_t* dqrow = p.dq + b * p.dqs0 + hq * p.dqs1 + (int64_t)qi * p.dqs2;
-  if (nblk == 0) {  // no visible key: dQ = 0
-    if (qi < p.Nq)
-      for (int d = 4 * hi; d < D; d += 8) *reinterpret_cast<u32x2_t*>(dqrow + d) = u32x2_t{};
-    return;  // uniform over the workgroup
-  }
-
-  // Q and dO rows of this lane's query as B operands (k-elements = head dim), and its
-  // (LSE log2 e, D_i); rows past Nq read as zero
+  // Q and dO rows of this lane's query as B operands (k-elements = head dim); rows past
+  // Nq read as zero.  The row's statistics: l2 = LSE log2 e (+inf for a row with no
+  // visible key or past Nq, so its P is exactly zero) and D_i = sum_d dO_id O_id, from
+  // the O row loaded in the same lane layout and the two halves' partial sums; both are
+  // stored (as LSE log2 e and -D_i) for the dK/dV kernel, for every row below Nq,
+  // including the rows of tiles that see no key.
   u32x4_t qf[T::KS], df[T::KS];
-  float l2 = 0.f, dd = 0.f;
+  float l2 = INFINITY, dd = 0.f;
   {
     const int rows = min(BR, p.Nq - q_wg0);
     const auto rq = make_rsrc(p.q + b * p.qs0 + hq * p.qs1 + (int64_t)q_wg0 * p.qs2,
                               rows_span(rows, p.qs2 * 2, D * 2));
     const auto rd = make_rsrc(p.dout + b * p.dos0 + hq * p.dos1 + (int64_t)q_wg0 * p.dos2,
                               rows_span(rows, p.dos2 * 2, D * 2));
+    const auto ro = make_rsrc(p.o + b * p.os0 + hq * p.os1 + (int64_t)q_wg0 * p.os2,
+                              rows_span(rows, p.os2 * 2, D * 2));
     const uint32_t oq = (uint32_t)((wave * 32 + l32) * p.qs2 * 2) + 16 * hi;
     const uint32_t od = (uint32_t)((wave * 32 + l32) * p.dos2 * 2) + 16 * hi;
+    const uint32_t oo = (uint32_t)((wave * 32 + l32) * p.os2 * 2) + 16 * hi;
+    float part = 0.f;
 #pragma unroll
     for (int s = 0; s < T::KS; ++s) {
-      qf[s] = buf_load16(rq, oq + 32 * s);
       df[s] = buf_load16(rd, od + 32 * s);
+      const u32x4_t o = buf_load16(ro, oo + 32 * s);
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        part += bf16_lo(o[w]) * bf16_lo(df[s][w]) + bf16_hi(o[w]) * bf16_hi(df[s][w]);
     }
+    dd = halves_sum(part);
     if (qi < p.Nq) {
       const int64_t row = ((int64_t)b * p.Hq + hq) * p.Nq + qi;
-      l2 = p.lse2[row];
-      dd = -p.negd[row];
-    } else {
-      l2 = INFINITY;  // padding rows: P = 0
+      const float L = p.lse[row];
+      l2 = L == -INFINITY ? INFINITY : L * kLog2e;
+      if (hi == 0) {
+        p.lse2[row] = l2;
+        p.negd[row] = -dd;
+      }
+    }
+    if (nblk > 0) {
+#pragma unroll
+      for (int s = 0; s < T::KS; ++s) qf[s] = buf_load16(rq, oq + 32 * s);
     }
     asm volatile("" ::: "memory");  // issue these before the ring loads below
+  }
+
+  // (formed where it is used, so it is not held across the block loop)
+  auto dq_row = [&]() { return p.dq + b * p.dqs0 + hq * p.dqs1 + (int64_t)qi * p.dqs2; };
+  if (nblk == 0) {  // no visible key: dQ = 0
+    if (qi < p.Nq) {
+      uint16_t* dqrow = dq_row();
+      for (int d = 4 * hi; d < D; d += 8) *reinterpret_cast<u32x2_t*>(dqrow + d) = u32x2_t{};
+    }
+    return;  // uniform over the workgroup
   }
   f32x16_t ndv;  // -D_i in every register: the start of each dP^T product without dropout
 #pragma unroll
@@ -835,6 +828,7 @@ bwd_q_kernel(BwdParams p) {
   // ---- dQ = scale * acc (lane = query row, register = head-dim element)
   if (qi < p.Nq) {
     const float sc = p.scale;
+    uint16_t* dqrow = dq_row();
 #pragma unroll
     for (int d = 0; d < T::DB; ++d)
 #pragma unroll
@@ -857,25 +851,23 @@ hipError_t launch(K kernel, int64_t grid, int block, const BwdParams& p, hipStre
 
 template <int D, bool DROP>
 hipError_t launch_all(BwdParams p, hipStream_t stream) {
-  const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
-  constexpr int RPB = 256 / (D / 8);
-  hipError_t e = launch(bwd_pre_kernel<D>, (rows + RPB - 1) / RPB, 256, p, stream);
-  if (e != hipSuccess) return e;
-  p.nkt = (p.Nk + kKvBC - 1) / kKvBC;
-  e = launch(bwd_kv_kernel<D, DROP>, (int64_t)p.nkt * p.Hkv * p.B, 64 * kKvWaves, p, stream);
-  if (e != hipSuccess) return e;
-  // without dropout: 256-row query tiles of 8 waves, the second four in the rotated
-  // order, on a four-slot ring (two blocks ahead); with dropout: 128-row tiles of 4 waves,
-  // two workgroups per compute unit, on a two-slot ring
+  // dQ first: it also writes the row statistics the dK/dV kernel reads.  Without dropout:
+  // 256-row query tiles of 8 waves, the second four in the rotated order, on a four-slot
+  // ring (two blocks ahead); with dropout: 128-row tiles of 4 waves, two workgroups per
+  // compute unit, on a two-slot ring
+  hipError_t e;
   if constexpr (DROP) {
     constexpr int NW = 4, NS = 2;
     const int64_t nqt = (p.Nq + 32 * NW - 1) / (32 * NW);
-    return launch(bwd_q_kernel<D, NW, NS, true>, nqt * p.Hq * p.B, 64 * NW, p, stream);
+    e = launch(bwd_q_kernel<D, NW, NS, true>, nqt * p.Hq * p.B, 64 * NW, p, stream);
   } else {
     constexpr int NW = 8, NS = 4;
     const int64_t nqt = (p.Nq + 32 * NW - 1) / (32 * NW);
-    return launch(bwd_q_kernel<D, NW, NS, false, true>, nqt * p.Hq * p.B, 64 * NW, p, stream);
+    e = launch(bwd_q_kernel<D, NW, NS, false, true>, nqt * p.Hq * p.B, 64 * NW, p, stream);
   }
+  if (e != hipSuccess) return e;
+  p.nkt = (p.Nk + kKvBC - 1) / kKvBC;
+  return launch(bwd_kv_kernel<D, DROP>, (int64_t)p.nkt * p.Hkv * p.B, 64 * kKvWaves, p, stream);
 }
 
 }  // namespace
