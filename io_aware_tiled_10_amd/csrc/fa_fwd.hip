@@ -467,15 +467,24 @@ fwd_bf16_kernel(FwdParams p) {
 }
 
 // fp32 inputs, D = 64: one lane per query row, K/V blocks of 32 keys broadcast from
-// LDS, fp32 FMA on the vector units (the small fp32 workload is launch-bound; the
-// matrix cores are reserved for the bf16 path).
-constexpr int kF32BR = 64, kF32BC = 32;
+// LDS, fp32 FMA on the vector units (the small fp32 workload is latency-bound; the
+// matrix cores are reserved for the bf16 path).  The NW waves of a workgroup share its
+// 64 query rows and split the key blocks among them (wave w takes blocks w, w + NW, ...,
+// each through its own LDS buffers), each keeping its own running (m, l, acc); at the
+// end the NW partial states of each row are merged through LDS by the LSE rule (the
+// same rule the split-KV decode merge applies), each wave finishing D / NW columns.
+constexpr int kF32BR = 64, kF32BC = 32, kF32Waves = 8;
 
-template <int D>
-__global__ void __launch_bounds__(64) fwd_f32_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) float ks[kF32BC][D];
-  __shared__ __attribute__((aligned(16))) float vs[kF32BC][D];
-  const int tid = threadIdx.x;
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW) fwd_f32_kernel(FwdParams p) {
+  static_assert(D % NW == 0, "the merge splits the columns evenly over the waves");
+  // K and V blocks of each wave; after the key loop the same memory holds the waves'
+  // accumulators, [wave][column][row]
+  __shared__ __attribute__((aligned(16))) float kvbuf[NW][2][kF32BC][D];
+  __shared__ float mlbuf[2][NW][kF32BR];
+  static_assert(sizeof(kvbuf) >= sizeof(float) * NW * D * kF32BR, "merge area");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   int t = xcd_contiguous(blockIdx.x, gridDim.x);
   const int gi = t % p.G;
@@ -500,7 +509,8 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdParams p) {
     kend = lim < kend ? lim : kend;
   }
   if (kend < 0) kend = 0;
-  const int qi = q_wg0 + tid;
+  const int nblk = (kend + kF32BC - 1) / kF32BC;
+  const int qi = q_wg0 + lane;
   const int last = p.causal ? min(lk - 1, qi + diag) : lk - 1;
 
   const float* qsrc = static_cast<const float*>(static_cast<const void*>(p.q));
@@ -516,21 +526,32 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdParams p) {
     acc[d] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
+  float (*ks)[D] = kvbuf[wave][0];
+  float (*vs)[D] = kvbuf[wave][1];
 
-  for (int key0 = 0; key0 < kend; key0 += kF32BC) {
-    __syncthreads();
-    for (int e = tid; e < kF32BC * D / 4; e += 64) {
-      const int row = e / (D / 4), col = 4 * (e % (D / 4));
-      const int key = key0 + row;
-      f32x4_t kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-      if (key < lk) {
-        kv = *reinterpret_cast<const f32x4_t*>(ksrc + (int64_t)key * p.ks2 + col);
-        vv = *reinterpret_cast<const f32x4_t*>(vsrc + (int64_t)key * p.vs2 + col);
+  // every wave runs the same number of trips (the barriers are shared); a trip past the
+  // wave's last block loads and computes nothing
+  const int trips = (nblk + NW - 1) / NW;
+  for (int it = 0; it < trips; ++it) {
+    const int blk = it * NW + wave;
+    const int key0 = blk * kF32BC;
+    const bool live = blk < nblk;
+    __syncthreads();  // the previous trip's reads of this wave's buffers are done
+    if (live) {
+      for (int e = lane; e < kF32BC * D / 4; e += 64) {
+        const int row = e / (D / 4), col = 4 * (e % (D / 4));
+        const int key = key0 + row;
+        f32x4_t kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+        if (key < lk) {
+          kv = *reinterpret_cast<const f32x4_t*>(ksrc + (int64_t)key * p.ks2 + col);
+          vv = *reinterpret_cast<const f32x4_t*>(vsrc + (int64_t)key * p.vs2 + col);
+        }
+        *reinterpret_cast<f32x4_t*>(&ks[row][col]) = kv;
+        *reinterpret_cast<f32x4_t*>(&vs[row][col]) = vv;
       }
-      *reinterpret_cast<f32x4_t*>(&ks[row][col]) = kv;
-      *reinterpret_cast<f32x4_t*>(&vs[row][col]) = vv;
     }
     __syncthreads();
+    if (!live) continue;
     float s[kF32BC];
     float mx = -INFINITY;
 #pragma unroll
@@ -558,14 +579,48 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdParams p) {
     m = m_new;
   }
 
+  // ---- merge: wave w's state of row `lane` -> LDS; wave w then finishes columns
+  //      [w D / NW, (w + 1) D / NW) of every row: M = max_w m_w, a_w = 2^((m_w - M) c)
+  //      (0 for a wave that saw no key), L = sum_w a_w l_w, O = sum_w a_w acc_w / L,
+  //      LSE = M scale + ln L (O = 0, LSE = -inf when L = 0)
+  __syncthreads();
+  float* accbuf = &kvbuf[0][0][0][0];
+#pragma unroll
+  for (int d = 0; d < D; ++d) accbuf[(wave * D + d) * kF32BR + lane] = acc[d];
+  mlbuf[0][wave][lane] = m;
+  mlbuf[1][wave][lane] = l;
+  __syncthreads();
+  float mw[NW], M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mw[w] = mlbuf[0][w][lane];
+    M = fmaxf(M, mw[w]);
+  }
+  float aw[NW], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    aw[w] = mw[w] == -INFINITY ? 0.f : fast_exp2((mw[w] - M) * c);
+    L += aw[w] * mlbuf[1][w][lane];
+  }
   if (qi < p.Nq) {
-    const float inv = l == 0.f ? 0.f : 1.f / l;
+    const float inv = L == 0.f ? 0.f : 1.f / L;
+    constexpr int DC = D / NW;
+    const int d0 = wave * DC;
     float* orow = static_cast<float*>(p.o) + b * p.os0 + hq * p.os1 + (int64_t)qi * p.os2;
 #pragma unroll
-    for (int d = 0; d < D; d += 4)
-      *reinterpret_cast<f32x4_t*>(orow + d) =
-          f32x4_t{acc[d] * inv, acc[d + 1] * inv, acc[d + 2] * inv, acc[d + 3] * inv};
-    if (p.lse) p.lse[b * p.lse_sb + hq * p.lse_sh + qi] = l == 0.f ? -INFINITY : m * p.scale + __logf(l);
+    for (int d = 0; d < DC; d += 4) {
+      f32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) x = fmaf(aw[w], accbuf[(w * D + d0 + d + e) * kF32BR + lane], x);
+        o[e] = x * inv;
+      }
+      *reinterpret_cast<f32x4_t*>(orow + d0 + d) = o;
+    }
+    if (p.lse && wave == 0)
+      p.lse[b * p.lse_sb + hq * p.lse_sh + qi] = L == 0.f ? -INFINITY : M * p.scale + __logf(L);
   }
 }
 
@@ -585,7 +640,7 @@ hipError_t launch_fwd(const FwdParams& p0, int in_dtype, int out_dtype, int D, h
     p.nqt = (p.Nq + kF32BR - 1) / kF32BR;
     const int64_t grid = (int64_t)p.nqt * p.Hq * p.B;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    return launch(fwd_f32_kernel<64>, (int)grid, 64, p, stream);
+    return launch(fwd_f32_kernel<64, kF32Waves>, (int)grid, 64 * kF32Waves, p, stream);
   }
   p.nqt = (p.Nq + kFwdBR - 1) / kFwdBR;
   const int64_t grid = (int64_t)p.nqt * p.Hq * p.B;
