@@ -103,7 +103,7 @@ fwd_bf16_kernel(FwdParams p) {
   using T = FwdTile<D, QK8>;
   static_assert(!QK8 || D == 128, "the E4M3 path is built for D = 128");
   static_assert(!(QK8 && DROP), "dropout is built for the bf16 path");
-  constexpr int BR = kFwdBR, BC = kFwdBC, NW = kFwdWaves, NS = kFwdSlots;
+  constexpr int BC = kFwdBC, NW = kFwdWaves, NS = kFwdSlots;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[T::LDS_BYTES];
   unsigned char* kring = lds;
   unsigned char* vring = lds + NS * T::KTBYTES;
@@ -117,12 +117,20 @@ fwd_bf16_kernel(FwdParams p) {
   // XCD receives every batch entry and sequences of different length (packed batches)
   // spread evenly over the XCDs.  Packed batches keep each group's ranks together: their
   // rank-0 tiles are empty for all but the longest sequences.
-  const TileId tid8 = tile_order(blockIdx.x, gridDim.x, p.B * p.Hkv, p.nqt, p.G, p.cu_q == nullptr);
+  // A tile holds the same RT = 256 / th query rows of th query heads of one GQA group
+  // (th = 1: 256 rows of one head).  Wave w takes head th_slot = w / (8 / th) of the tile
+  // and rows 32 (w % (8 / th)) ..; all waves of a tile share its key range, so a causal
+  // tile stops at the diagonal of its RT rows (with th = 4, 64 rows: a quarter of the
+  // masked work of a 256-row tile on the diagonal).
+  const int th = p.th, wph = NW / th;  // waves per head
+  const int RT = 32 * wph;             // query rows per tile
+  const int hs = wave / wph, ro = 32 * (wave % wph);
+  const TileId tid8 = tile_order(blockIdx.x, gridDim.x, p.B * p.Hkv, p.nqt, p.G / th, p.cu_q == nullptr);
   const int gi = tid8.gi, rank = tid8.rank;
   const int b = tid8.pair % p.B;
   const int hkv = tid8.pair / p.B;
   const int qt = p.causal ? p.nqt - 1 - rank : rank;
-  const int hq = hkv * p.G + gi;
+  const int hq = hkv * p.G + gi * th + hs;  // this wave's query head
 
   // this batch entry's query rows and valid keys; a packed batch takes them from the
   // offsets (clamped to the packed tensors) and shifts every row index by its first row
@@ -137,17 +145,17 @@ fwd_bf16_kernel(FwdParams p) {
     lk = lk < 0 ? 0 : (lk > p.Nk ? p.Nk : lk);
   }
   const int diag = lk - nq;  // key j visible to query i iff j <= i + diag
-  const int q_wg0 = qt * BR;
+  const int q_wg0 = qt * RT;
   if (q_wg0 >= nq) return;  // a tile past a short sequence of a packed batch (uniform)
   int kend = lk;
   if (p.causal) {
-    const int lim = q_wg0 + BR + diag;  // one past the last key the tile's last row sees
+    const int lim = q_wg0 + RT + diag;  // one past the last key the tile's last row sees
     kend = lim < kend ? lim : kend;
   }
   if (kend < 0) kend = 0;
   const int nblk = (kend + BC - 1) / BC;
 
-  const int qi = q_wg0 + wave * 32 + l32;  // this lane's query row
+  const int qi = q_wg0 + ro + l32;  // this lane's query row
 
   if (nblk == 0) {  // no visible key for any row of the tile: O = 0, LSE = -inf
     if (qi < nq) {
@@ -172,20 +180,21 @@ fwd_bf16_kernel(FwdParams p) {
   float dqw = 1.f;  // E4M3: the step of this wave's 64-row query block
   {
     const int64_t qpitch = p.qs2 * (QK8 ? 1 : 2);
+    // this wave's 32 rows of its head (rows past Nq read as zero)
     const unsigned char* qtile = reinterpret_cast<const unsigned char*>(p.q) +
-                                 (b * p.qs0 + hq * p.qs1 + (qr0 + q_wg0) * p.qs2) * (QK8 ? 1 : 2);
-    const auto rq = make_rsrc(qtile, rows_span(min(BR, nq - q_wg0), qpitch, T::KROWB));
+                                 (b * p.qs0 + hq * p.qs1 + (qr0 + q_wg0 + ro) * p.qs2) * (QK8 ? 1 : 2);
+    const auto rq = make_rsrc(qtile, rows_span(min(32, nq - q_wg0 - ro), qpitch, T::KROWB));
     if constexpr (QK8) {
-      const uint32_t off = (uint32_t)((wave * 32 + l32) * qpitch) + 32 * hi;
+      const uint32_t off = (uint32_t)(l32 * qpitch) + 32 * hi;
 #pragma unroll
       for (int s = 0; s < T::KS8; ++s)
         qf8[s] = cat8(buf_load16(rq, off + 64 * s), buf_load16(rq, off + 64 * s + 16));
       // (a wave whose rows all lie past Nq takes the last block's step; its rows are
       // never stored)
-      const int qblk = min((q_wg0 + 32 * wave) / 64, (nq + 63) / 64 - 1);
+      const int qblk = min((q_wg0 + ro) / 64, (nq + 63) / 64 - 1);
       dqw = p.q_scale[b * p.qsc_b + hq * p.qsc_h + qblk];
     } else {
-      const uint32_t off = (uint32_t)((wave * 32 + l32) * qpitch) + 16 * hi;
+      const uint32_t off = (uint32_t)(l32 * qpitch) + 16 * hi;
 #pragma unroll
       for (int s = 0; s < T::KS; ++s) qf[s] = buf_load16(rq, off + 32 * s);
     }
@@ -634,6 +643,22 @@ hipError_t launch(K kernel, int grid, int block, const FwdParams& p, hipStream_t
 
 }  // namespace
 
+// Tile shape of the bf16 kernels: a causal tile on the diagonal computes its whole last
+// key blocks for rows that see only part of them, so with GQA (query heads sharing a KV
+// head) a tile takes 64 rows of 4 heads (or 128 rows of 2) instead of 256 rows of one
+// head: the same K/V blocks per tile, a quarter of the masked work.  Sets p.th and
+// p.nqt; returns the workgroup count.
+int64_t bf16_grid(FwdParams& p) {
+  p.th = 1;
+  if (p.causal) {
+    if (p.G % 4 == 0) p.th = 4;
+    else if (p.G % 2 == 0) p.th = 2;
+  }
+  const int rt = kFwdBR / p.th;
+  p.nqt = (p.Nq + rt - 1) / rt;
+  return (int64_t)p.nqt * (p.Hq / p.th) * p.B;
+}
+
 hipError_t launch_fwd(const FwdParams& p0, int in_dtype, int out_dtype, int D, hipStream_t stream) {
   FwdParams p = p0;
   if (in_dtype == FA_F32) {
@@ -642,8 +667,7 @@ hipError_t launch_fwd(const FwdParams& p0, int in_dtype, int out_dtype, int D, h
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     return launch(fwd_f32_kernel<64, kF32Waves>, (int)grid, 64 * kF32Waves, p, stream);
   }
-  p.nqt = (p.Nq + kFwdBR - 1) / kFwdBR;
-  const int64_t grid = (int64_t)p.nqt * p.Hq * p.B;
+  const int64_t grid = bf16_grid(p);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const bool of32 = out_dtype == FA_F32;
   if (D == 128)
@@ -655,8 +679,7 @@ hipError_t launch_fwd(const FwdParams& p0, int in_dtype, int out_dtype, int D, h
 
 hipError_t launch_fwd_dropout(const FwdParams& p0, int out_dtype, int D, hipStream_t stream) {
   FwdParams p = p0;
-  p.nqt = (p.Nq + kFwdBR - 1) / kFwdBR;
-  const int64_t grid = (int64_t)p.nqt * p.Hq * p.B;
+  const int64_t grid = bf16_grid(p);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const bool of32 = out_dtype == FA_F32;
   if (D == 128)
@@ -668,8 +691,7 @@ hipError_t launch_fwd_dropout(const FwdParams& p0, int out_dtype, int D, hipStre
 
 hipError_t launch_fwd_fp8(const FwdParams& p0, int out_dtype, hipStream_t stream) {
   FwdParams p = p0;
-  p.nqt = (p.Nq + kFwdBR - 1) / kFwdBR;
-  const int64_t grid = (int64_t)p.nqt * p.Hq * p.B;
+  const int64_t grid = bf16_grid(p);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   return out_dtype == FA_F32
              ? launch(fwd_bf16_kernel<128, true, true>, (int)grid, 64 * kFwdWaves, p, stream)

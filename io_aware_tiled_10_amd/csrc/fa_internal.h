@@ -31,6 +31,7 @@ struct FwdParams {
   uint32_t drop_t, seed_lo, seed_hi;
   float drop_scale;
   int B, Hq, Hkv, Nq, Nk, G, nqt;  // packed batches: Nq = longest sequence
+  int th;  // bf16 forward: query heads of one GQA group that share a workgroup tile
   float scale, scale_log2;
   int causal;
 };
