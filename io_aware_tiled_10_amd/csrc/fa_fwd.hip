@@ -124,7 +124,12 @@ fwd_bf16_kernel(FwdParams p) {
   // masked work of a 256-row tile on the diagonal).
   const int th = p.th, wph = NW / th;  // waves per head
   const int RT = 32 * wph;             // query rows per tile
-  const int hs = wave / wph, ro = 32 * (wave % wph);
+  // Rows of the waves of a 256-row tile: the two waves that share a SIMD (waves w and
+  // w + 4) take row groups from opposite ends of the tile, so on the diagonal, where the
+  // waves of the lower rows need more key blocks than those of the upper rows, each SIMD
+  // carries about the same number of (wave, block) steps.
+  const int hs = wave / wph;
+  const int ro = 32 * (wph == 8 ? (wave < 4 ? wave : 11 - wave) : wave % wph);
   const TileId tid8 = tile_order(blockIdx.x, gridDim.x, p.B * p.Hkv, p.nqt, p.G / th, p.cu_q == nullptr);
   const int gi = tid8.gi, rank = tid8.rank;
   const int b = tid8.pair % p.B;
@@ -284,14 +289,19 @@ fwd_bf16_kernel(FwdParams p) {
   // One block: (s0, s1) hold the scores of block j (keys 64 j + [0, 32), + [32, 64));
   // the scores of block j + 1 are produced into (n0, n1).
   // `slot` is j % NS.
+  // `act`: false when every key of block j lies past the diagonal of all of this wave's
+  // rows (only in the steps after the unrolled loop, where the tile's last blocks cross
+  // the diagonal): the wave then skips the block's work, whose probabilities would all
+  // be exactly zero, and only issues its share of the ring loads and meets the barrier.
   auto step = [&](int j, auto slot, f32x16_t& s0, f32x16_t& s1, f32x16_t& n0, f32x16_t& n1,
-                  auto first) {
+                  auto first, bool act) {
     constexpr int sl = decltype(slot)::value;
     constexpr bool kFirst = decltype(first)::value;
     constexpr uint32_t vo = sl * T::TBYTES;
     // K_{j+3} and V_{j+2} into the slots of K_{j-1} and V_{j-2}, which are free
     dma_k(j + 3, (sl + 3) % NS);
     dma_v(j + 2, (sl + 2) % NS);
+    if (act) {
     float sq = 1.f;  // score units per MFMA unit of this block
     if constexpr (QK8) {
       sq = dqw * dk_next;
@@ -404,6 +414,7 @@ fwd_bf16_kernel(FwdParams p) {
       for (int ts = 0; ts < 4; ++ts)
         acc[d] = mfma32(u32x4_t{w[ts][0][0], w[ts][0][1], w[ts][1][0], w[ts][1][1]}, pf[ts], acc[d]);
     }
+    }  // act
 
     // the loads of blocks j + 2 (K) and j + 1 (V), issued one block ago, have landed
     // (only this block's may still be in flight); the barrier then publishes them and
@@ -431,17 +442,20 @@ fwd_bf16_kernel(FwdParams p) {
   // blocks per trip, so every slot index is a constant; the score registers alternate.
   static_assert(NS == 4, "the unrolled loop below walks four slots");
   using Later = std::false_type;
-  step(0, Slot<0>{}, sa0, sa1, sb0, sb1, std::true_type{});
+  step(0, Slot<0>{}, sa0, sa1, sb0, sb1, std::true_type{}, true);
   int j = 1;
   for (; j + 3 < nblk; j += 4) {
-    step(j, Slot<1>{}, sb0, sb1, sa0, sa1, Later{});
-    step(j + 1, Slot<2>{}, sa0, sa1, sb0, sb1, Later{});
-    step(j + 2, Slot<3>{}, sb0, sb1, sa0, sa1, Later{});
-    step(j + 3, Slot<0>{}, sa0, sa1, sb0, sb1, Later{});
+    step(j, Slot<1>{}, sb0, sb1, sa0, sa1, Later{}, true);
+    step(j + 1, Slot<2>{}, sa0, sa1, sb0, sb1, Later{}, true);
+    step(j + 2, Slot<3>{}, sb0, sb1, sa0, sa1, Later{}, true);
+    step(j + 3, Slot<0>{}, sa0, sa1, sb0, sb1, Later{}, true);
   }
-  if (j < nblk) step(j, Slot<1>{}, sb0, sb1, sa0, sa1, Later{});
-  if (j + 1 < nblk) step(j + 1, Slot<2>{}, sa0, sa1, sb0, sb1, Later{});
-  if (j + 2 < nblk) step(j + 2, Slot<3>{}, sb0, sb1, sa0, sa1, Later{});
+  // the last block any row of this wave sees (causal; a wave whose rows see no key
+  // keeps to the first block)
+  const int wlast = p.causal ? max(q_wg0 + ro + 31 + diag, 0) / BC : nblk - 1;
+  if (j < nblk) step(j, Slot<1>{}, sb0, sb1, sa0, sa1, Later{}, j <= wlast);
+  if (j + 1 < nblk) step(j + 1, Slot<2>{}, sa0, sa1, sb0, sb1, Later{}, j + 1 <= wlast);
+  if (j + 2 < nblk) step(j + 2, Slot<3>{}, sb0, sb1, sa0, sa1, Later{}, j + 2 <= wlast);
   FA_WAIT_VMCNT(0);  // the trailing loads (past the keys: zeros) write the ring too
 
   // ---- epilogue: O = acc / l once (times 1 / keep with dropout); LSE = m * scale + ln(l).
