@@ -30,6 +30,13 @@ SMALL = [
     ("single_row_single_key", 1, 1, 1, 1, 1, 128, False, None),
     ("single_row_causal", 1, 2, 1, 1, 129, 128, True, None),
     ("exact_tiles", 1, 2, 2, 256, 256, 128, True, None),
+    # several 256-row causal tiles, whose last steps skip blocks per wave, with the
+    # diagonal offset by Nk - Nq (blocks not aligned to the tile)
+    ("mha_causal_tiles_nq_lt_nk", 1, 2, 2, 1000, 1300, 128, True, None),
+    ("mha_causal_tiles_nq_gt_nk", 1, 2, 2, 1100, 700, 64, True, None),
+    # causal GQA tiles of 128 rows x 2 heads and of 64 rows x 4 heads
+    ("gqa2_causal_tiles", 1, 4, 2, 700, 700, 128, True, None),
+    ("gqa4_causal_tiles_kvlens", 2, 8, 2, 600, 650, 128, True, [650, 333]),
 ]
 
 
