@@ -338,10 +338,16 @@ class _Parity:
 
     def fwd(self, o, lse, o_ref, lse_ref, o_bf16: bool):
         self.n += 1
-        finite = bool(np.all(np.isfinite(o)) and np.all(np.isfinite(lse)))
+        finite = bool(np.all(np.isfinite(o)))
         err = np.abs(o - o_ref)
         excess = float((err - (TOL_O + (_half_ulp_bf16(o_ref) if o_bf16 else 0.0))).max())
-        el = float(np.abs(lse - lse_ref).max())
+        # a row with no visible key has LSE -inf on both sides; -inf must meet -inf
+        lse, lse_ref = np.asarray(lse, np.float64), np.asarray(lse_ref, np.float64)
+        both = np.isneginf(lse) & np.isneginf(lse_ref)
+        finite &= bool(np.array_equal(np.isneginf(lse), np.isneginf(lse_ref)) and np.all(np.isfinite(lse[~both])))
+        diff = np.zeros_like(lse)
+        diff[~both] = lse[~both] - lse_ref[~both]
+        el = float(np.abs(diff).max()) if lse.size else 0.0
         self._max("o_max_abs", err.max())
         self._max("lse_max_abs", el)
         self.worst["o_bound_excess"] = max(self.worst.get("o_bound_excess", -1.0), excess)
