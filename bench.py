@@ -50,6 +50,7 @@ import argparse
 import hashlib
 import json
 import math
+import re
 import os
 import sys
 import time
@@ -506,10 +507,18 @@ def ceilings():
     return res
 
 
+def _code_only(text: str) -> str:
+    """The source with comments and blank lines removed, so that a change to comments
+    alone does not retire a counter summary taken on the same machine code."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def sources_sha256(paths) -> str:
     h = hashlib.sha256()
     for p in paths:
-        h.update(open(p, "rb").read())
+        h.update(_code_only(open(p, encoding="utf-8").read()).encode())
     return h.hexdigest()
 
 
@@ -571,7 +580,7 @@ def write_traffic_summary(fetch_csv: str, write_csv: str, out: str) -> None:
         fh.write(f"- algorithmic bytes per launch: {algo} (ratio {total / algo:.2f})\n")
         fh.write(f"- kernel sources sha256: `{sources_sha256(FWD_KERNEL_SRCS)}`\n")
         fh.write("\nbench.py reports `roofline.traffic` from the HBM-bytes line only while the kernel "
-                 "sources hash to the value above.\n")
+                 "sources, comments and blank lines aside, hash to the value above.\n")
     print(f"wrote {out}: {total} bytes per launch", file=sys.stderr)
 
 

@@ -11,7 +11,9 @@
 //  * one workgroup = 8 waves = 256 query rows, one workgroup per compute unit (two
 //    waves per SIMD); each wave owns 32 rows outright (the article's "Warp级并行"
 //    principle: no reduction across waves).  A K/V block staged in LDS serves all 256
-//    rows, halving the L2 -> LDS traffic per FLOP against 128-row tiles;
+//    rows, halving the L2 -> LDS traffic per FLOP against 128-row tiles.  The rows are
+//    256 rows of one head, or, for a causal GQA group, 64 rows of 4 heads (128 of 2)
+//    that share the K/V head, so a tile on the diagonal stops sooner;
 //  * K/V blocks of 64 keys go from L2/HBM straight into LDS (LDS DMA: coalesced 1 KiB
 //    per wave instruction, no staging registers) through four-slot rings, with the
 //    16-byte slots of every row XOR-swizzled so that the operand reads are free of

@@ -114,3 +114,12 @@ def test_traffic_summary_round_trip(tmp_path):
     assert bench.traffic_for(bench.FWD_KERNEL_SRCS, str(stale)) is None
     assert bench.traffic_for(bench.FWD_KERNEL_SRCS, str(tmp_path / "missing.md")) is None
 
+
+
+def test_source_hash_ignores_comments_only(tmp_path):
+    a, b, c = tmp_path / "a.hip", tmp_path / "b.hip", tmp_path / "c.hip"
+    a.write_text("int f(int x) {\n  return x + 1;  // one more\n}\n")
+    b.write_text("// header\nint f(int x) {\n\n  return x + 1;  /* changed comment */\n}\n")
+    c.write_text("int f(int x) {\n  return x + 2;  // one more\n}\n")
+    assert bench.sources_sha256([str(a)]) == bench.sources_sha256([str(b)])
+    assert bench.sources_sha256([str(a)]) != bench.sources_sha256([str(c)])
