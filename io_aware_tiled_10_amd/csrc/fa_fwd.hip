@@ -120,10 +120,10 @@ fwd_bf16_kernel(FwdParams p) {
   // spread evenly over the XCDs.  Packed batches keep each group's ranks together: their
   // rank-0 tiles are empty for all but the longest sequences.
   // A tile holds the same RT = 256 / th query rows of th query heads of one GQA group
-  // (th = 1: 256 rows of one head).  Wave w takes head th_slot = w / (8 / th) of the tile
-  // and rows 32 (w % (8 / th)) ..; all waves of a tile share its key range, so a causal
-  // tile stops at the diagonal of its RT rows (with th = 4, 64 rows: a quarter of the
-  // masked work of a 256-row tile on the diagonal).
+  // (th = 1: 256 rows of one head).  Wave w takes head slot w / (8 / th) of the tile and
+  // one 32-row group of its rows (below); all waves of a tile share its key range, so a
+  // causal tile stops at the diagonal of its RT rows (with th = 4, 64 rows: a quarter of
+  // the masked work of a 256-row tile on the diagonal).
   const int th = p.th, wph = NW / th;  // waves per head
   const int RT = 32 * wph;             // query rows per tile
   // Rows of the waves of a 256-row tile: the two waves that share a SIMD (waves w and
