@@ -467,11 +467,49 @@ def cpu_baseline(gpu=None, budgets=(9.0, 4.0, 3.0)):
     return base, parity
 
 
+def mfma_ceiling(pattern: int, seconds: float = 1.0) -> float:
+    """TFLOP/s of libfa_ceiling's register-resident bf16 MFMA loop (the forward's
+    occupancy: 8-wave workgroups, one per compute unit, four launches per timing)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "io_aware_tiled_10_amd", "libfa_ceiling.so"))
+    lib.fa_ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_ceiling_mfma_flops.restype = ctypes.c_double
+    lib.fa_ceiling_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    wgs = torch.cuda.get_device_properties(DEV).multi_processor_count
+    out = torch.empty(wgs * 512, dtype=torch.float32, device=DEV)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run(iters, n=1):
+        for _ in range(n):
+            if lib.fa_ceiling_mfma(ctypes.c_void_p(out.data_ptr()), wgs, iters, pattern, ctypes.c_void_p(stream)):
+                raise RuntimeError("fa_ceiling_mfma failed")
+
+    def timed(iters, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        run(iters, n)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3
+
+    iters = 2000
+    run(iters)
+    t = timed(iters, 1)
+    iters = max(1, int(iters * seconds / 4 / max(t, 1e-6)))  # four launches of ~seconds / 4
+    run(iters)
+    t = timed(iters, 4)
+    return 4 * lib.fa_ceiling_mfma_flops(wgs, iters) / t / 1e12
+
+
 def ceilings():
-    """Achievable rates on this GPU for the same data statistics, for context: a library
-    bf16 GEMM (hipBLASLt via torch.matmul, 8192^3) on N(0,1) data and on all-ones data
-    (the sustained clock depends on the data), and a 2 GiB device-to-device copy."""
+    """Achievable rates on this GPU for the same data statistics, for context: the
+    matrix cores alone on register-resident operands (random-like and all-ones), a
+    library bf16 GEMM (hipBLASLt via torch.matmul, 8192^3) on N(0,1) data and on all-ones
+    data (the sustained clock depends on the data), and a 2 GiB device-to-device copy."""
     res = {}
+    res["mfma_loop_bf16_random_tflops"] = round(mfma_ceiling(0), 1)
+    res["mfma_loop_bf16_ones_tflops"] = round(mfma_ceiling(1), 1)
     n = 8192
     g = torch.Generator(device=DEV).manual_seed(0)
     for name, fill in (("random", None), ("ones", 1.0)):

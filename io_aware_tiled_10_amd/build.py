@@ -6,7 +6,9 @@ Each source under csrc/ is compiled to an object in _build/ (in parallel), then
 linked into io_aware_tiled_10_amd/libfa.so.  A second build of the same sources with
 FA_DEBUG_SYNC (every counted wait a full wait, every barrier draining the wave's
 loads first) is linked into libfa_debugsync.so: a race canary that the tests compare
-bit for bit with the first.  Always recompiles.
+bit for bit with the first.  The benchmark's measurement aid (fa_ceiling.hip, the
+sustained matrix-core rate on register-resident operands) is linked on its own into
+libfa_ceiling.so.  Always recompiles.
 """
 
 from __future__ import annotations
@@ -24,6 +26,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 LIB_DEBUG_SYNC = os.path.join(PKG, "libfa_debugsync.so")
+LIB_CEILING = os.path.join(PKG, "libfa_ceiling.so")
+CEILING_SOURCE = "fa_ceiling.hip"
 ARCH = "gfx950"
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_quant.hip"]
@@ -78,12 +82,13 @@ def _link(objs, out: str, verbose: bool) -> None:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    jobs = [(s, v) for v in ("", "debugsync") for s in SOURCES]
+    jobs = [(s, v) for v in ("", "debugsync") for s in SOURCES] + [(CEILING_SOURCE, "")]
     with ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
         objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
     n = len(SOURCES)
     _link(objs[:n], LIB, verbose)
-    _link(objs[n:], LIB_DEBUG_SYNC, verbose)
+    _link(objs[n:2 * n], LIB_DEBUG_SYNC, verbose)
+    _link(objs[2 * n:], LIB_CEILING, verbose)
     return LIB
 
 

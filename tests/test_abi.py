@@ -43,6 +43,27 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) <= exported
 
 
+def test_ceiling_library_exports_its_header_and_rejects_bad_arguments():
+    header = os.path.join(ROOT, "include", "fa_ceiling.h")
+    path = os.path.join(ROOT, "io_aware_tiled_10_amd", "libfa_ceiling.so")
+    text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+    declared = set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text))
+    assert declared == {"fa_ceiling_mfma", "fa_ceiling_mfma_flops"}
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    assert declared <= set(re.findall(r"\sT\s(fa_\w+)", out))
+    h = ctypes.CDLL(path)
+    h.fa_ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    h.fa_ceiling_mfma_flops.restype = ctypes.c_double
+    h.fa_ceiling_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    # invalid arguments return 1 before any launch
+    assert h.fa_ceiling_mfma(None, 1, 1, 0, None) == 1
+    assert h.fa_ceiling_mfma(FAKE, 0, 1, 0, None) == 1
+    assert h.fa_ceiling_mfma(FAKE, 1, 0, 0, None) == 1
+    assert h.fa_ceiling_mfma(FAKE, 1, 1, 2, None) == 1
+    # 8 waves x 16 products of 32 x 32 x 16 per trip
+    assert h.fa_ceiling_mfma_flops(3, 5) == 3 * 8 * 5 * 16 * 2 * 32 * 32 * 16
+
+
 def test_status_strings_and_version():
     h = fb.lib()
     for s in range(10):
