@@ -29,6 +29,9 @@ VARLEN = [
     ("ragged_noncausal_d128", [300, 64, 257], [450, 700, 33], 4, 1, 128, False),
     ("empty_q_and_k_seqs", [40, 0, 260, 30], [0, 50, 260, 90], 2, 2, 128, True),
     ("nq_gt_nk_masked_rows_d64", [200, 129], [70, 300], 4, 2, 64, True),
+    # groups of 4 query heads per KV head, causal: tiles of 64 rows x 4 heads
+    ("gqa4_causal_ragged", [700, 65, 300], [700, 65, 300], 8, 2, 128, True),
+    ("gqa4_causal_nq_ne_nk_d64", [150, 400], [300, 390], 8, 2, 64, True),
 ]
 
 
