@@ -14,7 +14,7 @@
 //  * one workgroup per (chunk, KV head, sequence), so every cached K/V byte is read
 //    from HBM exactly once and shared by the query heads of its GQA group, which
 //    occupy the 32 columns of the MFMA tile (padding columns are zero queries);
-//  * each of the 4 waves walks its own 32-key blocks of the chunk with no workgroup
+//  * each of the 2 waves walks its own 32-key blocks of the chunk with no workgroup
 //    barrier: the blocks stream straight from HBM into a private two-stage LDS ring
 //    (LDS DMA, no registers), one fully coalesced, non-temporal 1 KiB load per
 //    instruction, so the next block is in flight while the current one computes;
@@ -22,7 +22,9 @@
 //    MFMA operand reads are free of bank conflicts: K rows feed S^T = K q^T with plain
 //    16-byte reads, V feeds O^T += V^T P^T through transposing reads (no register
 //    shuffles and no second LDS pass);
-//  * the four waves' (m, l, acc) are merged through LDS at the end of the chunk;
+//  * the two waves' (m, l, acc) are merged through LDS at the end of the chunk; with
+//    64 KiB of LDS per workgroup two workgroups share a compute unit, so one's start
+//    (sequence length, q, first loads) overlaps the other's streaming;
 //  * chunks past a sequence's length exit at once; keys past it are never loaded;
 //  * a paged cache (interview answer, 高频追问 2: the blocked decode reads the paged KV
 //    blocks where they lie) changes only the descriptors: each 32-key block takes its
@@ -65,7 +67,7 @@ hipError_t decode_scratch(void** ptr) {
 
 namespace {
 
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 2;
 constexpr int kDecBlock = 32;  // keys per wave step
 
 template <int D>
@@ -91,7 +93,7 @@ struct DecTile {
 };
 
 template <int D, bool PAGED>
-__global__ void __launch_bounds__(256) decode_split_kernel(DecParams p) {
+__global__ void __launch_bounds__(64 * kDecWaves) decode_split_kernel(DecParams p) {
   using T = DecTile<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[T::LDS_BYTES];
 
@@ -158,26 +160,33 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecParams p) {
   float m = -INFINITY, l = 0.f;
   const float cl = p.scale_log2;
 
-  // block n of this wave covers keys [start + 32 (wave + 4 n), +32); past the chunk the
+  // block n of this wave covers keys [start + 32 (wave + 2 n), +32); past the chunk the
   // descriptor is empty, nothing is read and the stage is filled with zeros
   // Paged cache: the page ids of block n of this wave (one per 16-row half; both halves
   // name the same page when pages hold >= 32 rows), read from a register that lane
   // 2n + h filled from the block table with the q loads; -1 where no row of the chunk
-  // lies.  A chunk gives a wave at most 32 blocks (split_len <= 4096).
+  // lies.  A chunk gives a wave at most 64 blocks (split_len <= 4096): blocks 0-31 in
+  // vpage[0], blocks 32-63 in vpage[1].
   struct PageIds {
     int id[2];
   };
-  int vpage = -1;
+  int vpage[2] = {-1, -1};
   if constexpr (PAGED) {
-    const int row = start + kDecBlock * (wave + kDecWaves * (lane >> 1)) + 16 * (lane & 1);
-    if (row < end) vpage = p.table[s * p.table_stride + (row >> p.page_shift)];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int row = start + kDecBlock * (wave + kDecWaves * (32 * g + (lane >> 1))) + 16 * (lane & 1);
+      if (row < end) vpage[g] = p.table[s * p.table_stride + (row >> p.page_shift)];
+    }
   }
   auto pages_of = [&](int n) {
     PageIds r{{-1, -1}};
     if constexpr (PAGED) {
-      if (2 * n + 1 < 64) {
-        r.id[0] = __builtin_amdgcn_readlane(vpage, 2 * n);
-        r.id[1] = __builtin_amdgcn_readlane(vpage, 2 * n + 1);
+      if (n < 32) {
+        r.id[0] = __builtin_amdgcn_readlane(vpage[0], 2 * n);
+        r.id[1] = __builtin_amdgcn_readlane(vpage[0], 2 * n + 1);
+      } else if (n < 64) {
+        r.id[0] = __builtin_amdgcn_readlane(vpage[1], 2 * n - 64);
+        r.id[1] = __builtin_amdgcn_readlane(vpage[1], 2 * n - 63);
       }
     }
     return r;
@@ -301,7 +310,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecParams p) {
   }
   l = halves_sum(l);
 
-  // ---- merge the four waves' partial states
+  // ---- merge the waves' partial states
   __syncthreads();
   float* mrg = reinterpret_cast<float*>(lds);
   if (wave > 0) {
@@ -406,10 +415,10 @@ hipError_t launch_decode(const DecParams& p, int D, int out_dtype, hipStream_t s
     const dim3 grid((unsigned)n);
     const bool paged = p.table != nullptr;
     const hipError_t e =
-        D == 128 ? (paged ? launch(decode_split_kernel<128, true>, grid, dim3(256), p, stream)
-                          : launch(decode_split_kernel<128, false>, grid, dim3(256), p, stream))
-                 : (paged ? launch(decode_split_kernel<64, true>, grid, dim3(256), p, stream)
-                          : launch(decode_split_kernel<64, false>, grid, dim3(256), p, stream));
+        D == 128 ? (paged ? launch(decode_split_kernel<128, true>, grid, dim3(64 * kDecWaves), p, stream)
+                          : launch(decode_split_kernel<128, false>, grid, dim3(64 * kDecWaves), p, stream))
+                 : (paged ? launch(decode_split_kernel<64, true>, grid, dim3(64 * kDecWaves), p, stream)
+                          : launch(decode_split_kernel<64, false>, grid, dim3(64 * kDecWaves), p, stream));
     if (e != hipSuccess) return e;
   }
   const dim3 mgrid(p.Bs * p.Hq);

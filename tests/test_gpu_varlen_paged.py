@@ -93,6 +93,9 @@ PAGED = [
     ("p64_rowmajor", 8, 2, 128, [64, 65, 1000, 4097], 64, 1024, True, torch.bfloat16),
     ("p256_d64_mha", 4, 4, 64, [5, 255, 256, 257, 3000], 256, 256, False, torch.float32),
     ("p16_d64_rowmajor_zero_len", 8, 1, 64, [0, 50, 0, 17], 16, 128, True, torch.float32),
+    # 4096-key chunks: a wave's blocks 32-63 take their pages from the second page-id register
+    ("p16_d128_split4096", 8, 2, 128, [1, 2049, 4095, 4096, 4097, 9000], 16, 4096, False, torch.float32),
+    ("p128_d64_split4096", 8, 2, 64, [2100, 4096, 8191], 128, 4096, True, torch.bfloat16),
 ]
 
 
