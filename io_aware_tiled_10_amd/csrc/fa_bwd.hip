@@ -129,7 +129,7 @@ bwd_kv_kernel(BwdParams p) {
   const int kg = wave & 3;        // key group
   const int l32 = lane & 31, hi = lane >> 5;
 
-  const TileId tix = tile_order(blockIdx.x, gridDim.x, p.B * p.Hkv, p.nkt, 1);
+  const TileId tix = tile_order(blockIdx.x, gridDim.x, p.B * p.Hkv, p.nkt, 1, true, p.gsz);
   const int kt = tix.rank;
   const int hkv = tix.pair % p.Hkv;
   const int b = tix.pair / p.Hkv;
@@ -560,7 +560,7 @@ bwd_q_kernel(BwdParams p) {
 
   // tile: ordered as the forward's (heavy causal tiles first inside each XCD's groups)
   const int nqt = (p.Nq + BR - 1) / BR;
-  const TileId tix = tile_order(blockIdx.x, gridDim.x, p.B * p.Hkv, nqt, p.G);
+  const TileId tix = tile_order(blockIdx.x, gridDim.x, p.B * p.Hkv, nqt, p.G, true, p.gsz);
   const int gi = tix.gi, rank = tix.rank;
   const int hkv = tix.pair % p.Hkv;
   const int b = tix.pair / p.Hkv;
@@ -854,19 +854,33 @@ hipError_t launch_all(BwdParams p, hipStream_t stream) {
   // dQ first: it also writes the row statistics the dK/dV kernel reads.  Without dropout:
   // 256-row query tiles of 8 waves, the second four in the rotated order, on a four-slot
   // ring (two blocks ahead); with dropout: 128-row tiles of 4 waves, two workgroups per
-  // compute unit, on a two-slot ring
+  // compute unit, on a two-slot ring.
+  // Each kernel's XCDs take the (batch entry, KV head) groups a few at a time, so that the
+  // tiles in flight on an XCD share few groups' tensors in its L2: one group at a time
+  // when every tile does the same work (non-causal), else enough groups for four tiles
+  // per workgroup slot of the XCD's 32 compute units, so the longest-first order inside
+  // each batch of groups still balances (with two tiles per slot the B2 H16 N4096 causal
+  // backward ran 2-3 % slower).
+  auto group_size = [&](int64_t tiles_per_group, int slots_per_cu) {
+    if (!p.causal) return 1;
+    const int64_t want = 4 * 32 * slots_per_cu;
+    return (int)((want + tiles_per_group - 1) / tiles_per_group);
+  };
   hipError_t e;
   if constexpr (DROP) {
     constexpr int NW = 4, NS = 2;
     const int64_t nqt = (p.Nq + 32 * NW - 1) / (32 * NW);
+    p.gsz = group_size(nqt * p.G, 2);
     e = launch(bwd_q_kernel<D, NW, NS, true>, nqt * p.Hq * p.B, 64 * NW, p, stream);
   } else {
     constexpr int NW = 8, NS = 4;
     const int64_t nqt = (p.Nq + 32 * NW - 1) / (32 * NW);
+    p.gsz = group_size(nqt * p.G, 1);
     e = launch(bwd_q_kernel<D, NW, NS, false, true>, nqt * p.Hq * p.B, 64 * NW, p, stream);
   }
   if (e != hipSuccess) return e;
   p.nkt = (p.Nk + kKvBC - 1) / kKvBC;
+  p.gsz = group_size(p.nkt, 1);
   return launch(bwd_kv_kernel<D, DROP>, (int64_t)p.nkt * p.Hkv * p.B, 64 * kKvWaves, p, stream);
 }
 

@@ -78,15 +78,17 @@ __device__ __forceinline__ int xcd_contiguous(int id, int total) {
 // Tile order for a grid of npair groups (batch entry, KV head) x nrank ranks x ng heads
 // (total = npair * nrank * ng).  Each XCD receives a contiguous range of whole groups, so
 // the tiles that share a group's K/V share that XCD's L2.  When the groups split evenly
-// over the XCDs, the rank varies slowest inside each XCD's range: every XCD dispatches
-// the rank-0 tiles of all its groups first, then rank 1, ..., which with rank 0 the
-// heaviest gives a longest-first schedule.  Otherwise (or without rank_major) ranks vary
-// right after the heads.
+// over the XCDs, each XCD takes its groups gsz at a time (all of them when gsz <= 0), and
+// inside such a batch of groups the rank varies slowest: the rank-0 tiles of the batch
+// first, then rank 1, ..., which with rank 0 the heaviest gives a longest-first schedule.
+// A small gsz keeps few groups' K/V in flight on an XCD at once (gsz = 1: one group's
+// tiles after another's), so that they stay in its L2.  Otherwise (or without
+// rank_major) ranks vary right after the heads.
 struct TileId {
   int gi, rank, pair;
 };
 __device__ __forceinline__ TileId tile_order(int id, int total, int npair, int nrank, int ng,
-                                             bool rank_major = true) {
+                                             bool rank_major = true, int gsz = 0) {
   const int t = xcd_contiguous(id, total);
   TileId r;
   if (rank_major && npair % kNumXcd == 0) {
@@ -95,8 +97,13 @@ __device__ __forceinline__ TileId tile_order(int id, int total, int npair, int n
     int u = t - x * span;
     r.gi = u % ng;
     u /= ng;
-    r.rank = u / per;
-    r.pair = x * per + u % per;
+    // groups of gsz consecutive pairs (the last one may be smaller), one after another;
+    // rank-major inside each group
+    const int gs = (gsz <= 0 || gsz > per) ? per : gsz;
+    const int g = u / (gs * nrank), w = u - g * gs * nrank;
+    const int gl = min(gs, per - g * gs);
+    r.rank = w / gl;
+    r.pair = x * per + g * gs + w % gl;
   } else {
     r.gi = t % ng;
     const int u = t / ng;

@@ -132,7 +132,7 @@ fwd_bf16_kernel(FwdParams p) {
   // carries about the same number of (wave, block) steps.
   const int hs = wave / wph;
   const int ro = 32 * (wph == 8 ? (wave < 4 ? wave : 11 - wave) : wave % wph);
-  const TileId tid8 = tile_order(blockIdx.x, gridDim.x, p.B * p.Hkv, p.nqt, p.G / th, p.cu_q == nullptr);
+  const TileId tid8 = tile_order(blockIdx.x, gridDim.x, p.B * p.Hkv, p.nqt, p.G / th, p.cu_q == nullptr, p.gsz);
   const int gi = tid8.gi, rank = tid8.rank;
   const int b = tid8.pair % p.B;
   const int hkv = tid8.pair / p.B;
@@ -672,6 +672,11 @@ int64_t bf16_grid(FwdParams& p) {
   }
   const int rt = kFwdBR / p.th;
   p.nqt = (p.Nq + rt - 1) / rt;
+  // (batch entry, KV head) groups an XCD works through at a time: one when every tile
+  // does the same work (non-causal), else enough for two tiles per compute unit of the
+  // XCD (32), so the longest-first order inside a batch of groups still balances
+  const int per_pair = p.nqt * (p.G / p.th);
+  p.gsz = p.causal ? (2 * 32 + per_pair - 1) / per_pair : 1;
   return (int64_t)p.nqt * (p.Hq / p.th) * p.B;
 }
 

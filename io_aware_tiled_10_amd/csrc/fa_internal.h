@@ -32,6 +32,7 @@ struct FwdParams {
   float drop_scale;
   int B, Hq, Hkv, Nq, Nk, G, nqt;  // packed batches: Nq = longest sequence
   int th;  // bf16 forward: query heads of one GQA group that share a workgroup tile
+  int gsz; // bf16 forward: (batch entry, KV head) groups an XCD takes at a time
   float scale, scale_log2;
   int causal;
 };
@@ -63,6 +64,7 @@ struct BwdParams {
   int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2, dos0, dos1, dos2;
   int64_t dqs0, dqs1, dqs2, dks0, dks1, dks2, dvs0, dvs1, dvs2;
   int B, Hq, Hkv, Nq, Nk, G, nkt;
+  int gsz;  // (batch entry, KV head) groups an XCD takes at a time, per kernel
   float scale, scale_log2;
   int causal;
   uint32_t drop_t, seed_lo, seed_hi;  // dropout as in the forward (drop_t == 0: none)
