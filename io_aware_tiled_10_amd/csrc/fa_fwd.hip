@@ -649,6 +649,176 @@ __global__ void __launch_bounds__(64 * NW) fwd_f32_kernel(FwdParams p) {
   }
 }
 
+// fp32 forward for small grids (fewer 64-row tiles than two per compute unit, as in the
+// B1 H2 N256 workload, where the kernel above would leave all but a few compute units idle):
+// a workgroup of 256 threads takes a tile of TR = 16 query rows, and thread (row r, subset s)
+// keeps the running (m, l, acc) of row r over the keys j = s (mod NS), NS = 16, so each row's
+// work is spread over 16 threads and the grid has four times as many workgroups.  K and V
+// come through LDS in chunks of KC = 128 keys, each row padded by 16 bytes so that the keys a
+// wave reads at once lie in different banks.  At the end the NS partial states of each row
+// are merged through LDS by the LSE rule, thread (r, s) finishing columns D / NS * s .. of
+// row r.
+constexpr int kF32SmallThreads = 256, kF32SmallBR = 16, kF32KC = 128;
+
+template <int D>
+__global__ void __launch_bounds__(kF32SmallThreads) fwd_f32_small_kernel(FwdParams p) {
+  constexpr int TR = kF32SmallBR, NS = kF32SmallThreads / TR, KC = kF32KC, RP = D + 4, KI = KC / NS, CW = D / NS;
+  constexpr int NLD = KC * D / 4 / kF32SmallThreads;  // 16-byte loads per thread per tensor and chunk
+  static_assert(CW % 4 == 0 && KC % NS == 0 && NLD * 4 * kF32SmallThreads == KC * D, "tile shape");
+  // K and V chunks; after the key loop the same memory holds the threads' accumulators,
+  // subset s at [s * SD], column d, row r at [s * SD + d * TR + r]
+  constexpr int SD = D * TR + 4;
+  __shared__ __attribute__((aligned(16))) float kv[2][KC][RP];
+  __shared__ float mlbuf[2][NS][TR];
+  static_assert(sizeof(kv) >= sizeof(float) * NS * SD, "merge area");
+  const int tid = threadIdx.x;
+  const int r = tid % TR, s = tid / TR;
+
+  int t = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int gi = t % p.G;
+  t /= p.G;
+  const int rank = t % p.nqt;
+  t /= p.nqt;
+  const int hkv = t % p.Hkv;
+  const int b = t / p.Hkv;
+  const int qt = p.causal ? p.nqt - 1 - rank : rank;
+  const int hq = hkv * p.G + gi;
+
+  int lk = p.Nk;
+  if (p.kv_lens) {
+    lk = p.kv_lens[b];
+    lk = lk < 0 ? 0 : (lk > p.Nk ? p.Nk : lk);
+  }
+  const int diag = lk - p.Nq;
+  const int q_wg0 = qt * TR;
+  int kend = lk;
+  if (p.causal) {
+    const int lim = q_wg0 + TR + diag;
+    kend = lim < kend ? lim : kend;
+  }
+  if (kend < 0) kend = 0;
+  const int qi = q_wg0 + r;
+  const int last = p.causal ? min(lk - 1, qi + diag) : lk - 1;
+
+  const float* qsrc = static_cast<const float*>(static_cast<const void*>(p.q));
+  const float* ksrc = static_cast<const float*>(static_cast<const void*>(p.k)) + b * p.ks0 + hkv * p.ks1;
+  const float* vsrc = static_cast<const float*>(static_cast<const void*>(p.v)) + b * p.vs0 + hkv * p.vs1;
+
+  float q[D], acc[D];
+  const float c = p.scale_log2;
+  const float* qrow = qsrc + b * p.qs0 + hq * p.qs1 + (int64_t)qi * p.qs2;
+#pragma unroll
+  for (int d = 0; d < D; d += 4) {
+    const f32x4_t v4 = qi < p.Nq ? *reinterpret_cast<const f32x4_t*>(qrow + d) : f32x4_t{};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      q[d + e] = v4[e];
+      acc[d + e] = 0.f;
+    }
+  }
+  float m = -INFINITY, l = 0.f;
+
+  for (int c0 = 0; c0 < kend; c0 += KC) {
+    // the chunk's loads are all issued before any is stored, so their latencies overlap
+    f32x4_t k4[NLD], v4[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int e = tid + kF32SmallThreads * i;
+      const int key = c0 + e / (D / 4), col = 4 * (e % (D / 4));
+      k4[i] = v4[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (key < lk) {
+        k4[i] = *reinterpret_cast<const f32x4_t*>(ksrc + (int64_t)key * p.ks2 + col);
+        v4[i] = *reinterpret_cast<const f32x4_t*>(vsrc + (int64_t)key * p.vs2 + col);
+      }
+    }
+    __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int e = tid + kF32SmallThreads * i;
+      const int row = e / (D / 4), col = 4 * (e % (D / 4));
+      *reinterpret_cast<f32x4_t*>(&kv[0][row][col]) = k4[i];
+      *reinterpret_cast<f32x4_t*>(&kv[1][row][col]) = v4[i];
+    }
+    __syncthreads();
+    // this thread's keys of the chunk: rows s, s + NS, ..., each against query row qi
+    float sc[KI];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int row = s + NS * i;
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; d += 4) {
+        const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(&kv[0][row][d]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dot = fmaf(q[d + e], k4[e], dot);
+      }
+      sc[i] = c0 + row > last ? -INFINITY : dot;
+      mx = fmaxf(mx, sc[i]);
+    }
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2((m - m_use) * c);
+    const float mc = m_use * c;
+    l *= alpha;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] *= alpha;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int row = s + NS * i;
+      const float pj = fast_exp2(fmaf(sc[i], c, -mc));
+      l += pj;
+#pragma unroll
+      for (int d = 0; d < D; d += 4) {
+        const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(&kv[1][row][d]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[d + e] = fmaf(pj, v4[e], acc[d + e]);
+      }
+    }
+    m = m_new;
+  }
+
+  // ---- merge: thread (r, s)'s state -> LDS; thread (r, s) then finishes columns CW s ..
+  //      CW s + CW - 1 of row r: M = max_s' m_s', a_s' = 2^((m_s' - M) c) (0 for a subset
+  //      that saw no key), L = sum_s' a_s' l_s', O = sum_s' a_s' acc_s' / L, LSE = M scale
+  //      + ln L (O = 0, LSE = -inf when L = 0)
+  __syncthreads();
+  float* accbuf = &kv[0][0][0];
+#pragma unroll
+  for (int d = 0; d < D; ++d) accbuf[s * SD + d * TR + r] = acc[d];
+  mlbuf[0][s][r] = m;
+  mlbuf[1][s][r] = l;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NS; ++w) M = fmaxf(M, mlbuf[0][w][r]);
+  float aw[NS], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < NS; ++w) {
+    const float mw = mlbuf[0][w][r];
+    aw[w] = mw == -INFINITY ? 0.f : fast_exp2((mw - M) * c);
+    L += aw[w] * mlbuf[1][w][r];
+  }
+  if (qi < p.Nq) {
+    const float inv = L == 0.f ? 0.f : 1.f / L;
+    float* orow = static_cast<float*>(p.o) + b * p.os0 + hq * p.os1 + (int64_t)qi * p.os2;
+#pragma unroll
+    for (int d = CW * s; d < CW * s + CW; d += 4) {
+      f32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = 0.f;
+#pragma unroll
+        for (int w = 0; w < NS; ++w) x = fmaf(aw[w], accbuf[w * SD + (d + e) * TR + r], x);
+        o[e] = x * inv;
+      }
+      *reinterpret_cast<f32x4_t*>(orow + d) = o;
+    }
+    if (p.lse && s == 0)
+      p.lse[b * p.lse_sb + hq * p.lse_sh + qi] = L == 0.f ? -INFINITY : M * p.scale + __logf(L);
+  }
+}
+
 template <typename K>
 hipError_t launch(K kernel, int grid, int block, const FwdParams& p, hipStream_t stream) {
   FwdParams local = p;
@@ -683,10 +853,16 @@ int64_t bf16_grid(FwdParams& p) {
 hipError_t launch_fwd(const FwdParams& p0, int in_dtype, int out_dtype, int D, hipStream_t stream) {
   FwdParams p = p0;
   if (in_dtype == FA_F32) {
-    p.nqt = (p.Nq + kF32BR - 1) / kF32BR;
+    // 64-row tiles of eight waves when they give every compute unit two workgroups,
+    // else 16-row tiles whose rows are each spread over 16 threads
+    const int64_t tiles64 = (int64_t)((p.Nq + kF32BR - 1) / kF32BR) * p.Hq * p.B;
+    const bool small = tiles64 < 2 * 256;
+    const int tr = small ? kF32SmallBR : kF32BR;
+    p.nqt = (p.Nq + tr - 1) / tr;
     const int64_t grid = (int64_t)p.nqt * p.Hq * p.B;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    return launch(fwd_f32_kernel<64, kF32Waves>, (int)grid, 64 * kF32Waves, p, stream);
+    return small ? launch(fwd_f32_small_kernel<64>, (int)grid, kF32SmallThreads, p, stream)
+                 : launch(fwd_f32_kernel<64, kF32Waves>, (int)grid, 64 * kF32Waves, p, stream);
   }
   const int64_t grid = bf16_grid(p);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;

@@ -97,6 +97,29 @@ def test_fwd_fp32_ragged(causal):
     assert assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, False) < 1e-5
 
 
+# The fp32 forward takes 16-row tiles (each row over 16 threads) when 64-row tiles would
+# give fewer than two per compute unit, else 64-row tiles of eight waves: these shapes
+# (B1 H64 GQA 8:1, 512 and 520 rows, 5 and 9 row tiles of 64 past 512 in all) take the
+# second path, with a ragged tail and Nq != Nk.
+FP32_WIDE = [
+    ("h64_n512", 64, 8, 512, 512, False),
+    ("h64_n520_causal", 64, 8, 520, 520, True),
+    ("h64_nq520_nk700_causal", 64, 8, 520, 700, True),
+]
+
+
+@pytest.mark.parametrize("case", FP32_WIDE, ids=[c[0] for c in FP32_WIDE])
+def test_fwd_fp32_many_tiles(case):
+    name, Hq, Hkv, Nq, Nk, causal = case
+    say(f"fwd fp32 {name}")
+    x = inputs.attention_inputs(1, Hq, Hkv, Nq, Nk, 64, "fp32", seed=11)
+    q, k, v = (to_dev(a, torch.float32) for a in (x.q, x.k, x.v))
+    o, lse = fa.fwd(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(x.q, x.k, x.v, None, causal)
+    assert assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, False) < 1e-5
+
+
 def test_fwd_gqa_equals_mha_with_repeated_kv():
     x = inputs.attention_inputs(1, 8, 2, 200, 200, 128, "bf16", seed=5)
     q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
