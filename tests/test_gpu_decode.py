@@ -36,6 +36,11 @@ SMALL = [
     ("mha_d64", 4, 4, 64, [5, 64, 300, 3000], 256, torch.float32),
     ("mqa_40_heads_two_head_blocks", 40, 1, 128, [1, 77, 2500], 512, torch.float32),
     ("zero_length_sequence", 8, 2, 128, [0, 50, 0], 128, torch.float32),
+    # long chunks: each of a workgroup's two waves walks up to 64 (split 4096) or 128
+    # (split 8192) 32-key blocks; and a chunk length that is not a power of two
+    ("gqa4_d128_split4096", 8, 2, 128, [1, 4095, 4096, 4097, 9000], 4096, torch.bfloat16),
+    ("gqa8_d64_split8192", 16, 2, 64, [383, 8191, 8192, 8193, 20000], 8192, torch.float32),
+    ("gqa4_d128_split384", 8, 2, 128, [383, 384, 385, 1000, 3000], 384, torch.float32),
 ]
 
 
