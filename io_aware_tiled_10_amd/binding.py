@@ -225,35 +225,39 @@ def _scale(scale: Optional[float], d: int) -> float:
 # these checks turn a mismatch into a ValueError before any library call
 # ----------------------------------------------------------------------------------
 
-def _need(cond: bool, msg: str) -> None:
+def _need(cond: bool, msg) -> None:
+    """Raise ValueError(msg) unless cond; msg may be a callable that builds the message,
+    so that a message with formatted values costs nothing when the check passes."""
     if not cond:
-        raise ValueError(msg)
+        raise ValueError(msg() if callable(msg) else msg)
 
 
 def _same_device(ref: torch.Tensor, **named) -> None:
     for name, t in named.items():
         if t is not None:
-            _need(t.device == ref.device, f"{name} is on {t.device}, expected {ref.device}")
+            _need(t.device == ref.device, lambda: f"{name} is on {t.device}, expected {ref.device}")
 
 
 def _on_gpu(ref: torch.Tensor) -> None:
-    _need(ref.device.type == "cuda", f"tensors must be on a GPU device, got {ref.device}")
+    _need(ref.device.type == "cuda", lambda: f"tensors must be on a GPU device, got {ref.device}")
 
 
 def _check_dtype(t: torch.Tensor, name: str, dtypes) -> None:
-    _need(t.dtype in dtypes, f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
+    _need(t.dtype in dtypes, lambda: f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
 
 
 def _check_shape(t: torch.Tensor, name: str, shape) -> None:
-    _need(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    _need(tuple(t.shape) == tuple(shape),
+          lambda: f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 def _check_int32_vec(t: Optional[torch.Tensor], name: str, n: int, ref: torch.Tensor) -> None:
     if t is None:
         return
     _check_dtype(t, name, (torch.int32,))
-    _need(t.dim() == 1 and t.numel() == n, f"{name} must be a 1-D tensor of {n} elements, got shape {tuple(t.shape)}")
-    _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(t.dim() == 1 and t.numel() == n,
+          lambda: f"{name} must be a 1-D tensor of {n} elements, got shape {tuple(t.shape)}")
+    _need(t.is_contiguous(), lambda: f"{name} must be contiguous")
     _same_device(ref, **{name: t})
 
 
@@ -262,7 +266,7 @@ def _check_f32_contig(t: Optional[torch.Tensor], name: str, shape, ref: torch.Te
         return
     _check_dtype(t, name, (torch.float32,))
     _check_shape(t, name, shape)
-    _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(t.is_contiguous(), lambda: f"{name} must be contiguous")
     _same_device(ref, **{name: t})
 
 
@@ -274,11 +278,11 @@ def _check_out(t: torch.Tensor, name: str, shape, dtypes, ref: torch.Tensor) -> 
 
 def _check_inputs(dtypes, ref_name: str, ref: torch.Tensor, ndim: int, **named) -> None:
     """Every named tensor: ``ndim`` dimensions, ref's dtype (one of ``dtypes``), ref's device."""
-    _need(ref.dim() == ndim, f"{ref_name} must have {ndim} dimensions, got {ref.dim()}")
+    _need(ref.dim() == ndim, lambda: f"{ref_name} must have {ndim} dimensions, got {ref.dim()}")
     _check_dtype(ref, ref_name, dtypes)
     for name, t in named.items():
-        _need(t.dim() == ndim, f"{name} must have {ndim} dimensions, got {t.dim()}")
-        _need(t.dtype == ref.dtype, f"{name} has dtype {t.dtype}, {ref_name} has {ref.dtype}")
+        _need(t.dim() == ndim, lambda: f"{name} must have {ndim} dimensions, got {t.dim()}")
+        _need(t.dtype == ref.dtype, lambda: f"{name} has dtype {t.dtype}, {ref_name} has {ref.dtype}")
     _same_device(ref, **named)
 
 
@@ -323,9 +327,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
 
 def _check_fwd_inputs(q, k, v, kv_lens) -> None:
     _check_inputs(_DT, "q", q, 4, k=k, v=v)
-    _need(k.shape == v.shape, f"k {tuple(k.shape)} and v {tuple(v.shape)} differ in shape")
+    _need(k.shape == v.shape, lambda: f"k {tuple(k.shape)} and v {tuple(v.shape)} differ in shape")
     _need(k.shape[0] == q.shape[0] and k.shape[3] == q.shape[3],
-          f"k/v {tuple(k.shape)} do not match q {tuple(q.shape)} in batch or head dim")
+          lambda: f"k/v {tuple(k.shape)} do not match q {tuple(q.shape)} in batch or head dim")
     _check_int32_vec(kv_lens, "kv_lens", q.shape[0], q)
 
 
@@ -512,9 +516,9 @@ def bwd_dropout(q, k, v, o, do, lse, p_drop: float, seed: int, causal: bool = Fa
 
 def _check_bwd_inputs(q, k, v, o, do, lse, kv_lens) -> None:
     _check_inputs((torch.bfloat16,), "q", q, 4, k=k, v=v, o=o, do=do)
-    _need(k.shape == v.shape, f"k {tuple(k.shape)} and v {tuple(v.shape)} differ in shape")
+    _need(k.shape == v.shape, lambda: f"k {tuple(k.shape)} and v {tuple(v.shape)} differ in shape")
     _need(k.shape[0] == q.shape[0] and k.shape[3] == q.shape[3],
-          f"k/v {tuple(k.shape)} do not match q {tuple(q.shape)} in batch or head dim")
+          lambda: f"k/v {tuple(k.shape)} do not match q {tuple(q.shape)} in batch or head dim")
     _check_shape(o, "o", q.shape)
     _check_shape(do, "do", q.shape)
     _need(lse is not None, "lse (the forward's log-sum-exp) is required")
@@ -596,7 +600,7 @@ def _check_decode_inputs(q, k_cache, v_cache, seq_lens) -> None:
     _same_device(q, k_cache=k_cache)
     _need(k_cache.shape == v_cache.shape, "k_cache and v_cache differ in shape")
     _need(k_cache.shape[0] == q.shape[0] and k_cache.shape[3] == q.shape[2],
-          f"caches {tuple(k_cache.shape)} do not match q {tuple(q.shape)} in sequences or head dim")
+          lambda: f"caches {tuple(k_cache.shape)} do not match q {tuple(q.shape)} in sequences or head dim")
     _need(seq_lens is not None, "seq_lens is required")
     _check_int32_vec(seq_lens, "seq_lens", q.shape[0], q)
 
@@ -640,7 +644,7 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, max_len: int, split
     _need(k_pages.shape[3] == q.shape[2], "the pools' head dim differs from q's")
     _check_dtype(block_table, "block_table", (torch.int32,))
     _need(block_table.dim() == 2 and block_table.shape[0] == q.shape[0],
-          f"block_table must be [Bs, W] with Bs = {q.shape[0]}, got {tuple(block_table.shape)}")
+          lambda: f"block_table must be [Bs, W] with Bs = {q.shape[0]}, got {tuple(block_table.shape)}")
     _same_device(q, block_table=block_table)
     _check_int32_vec(seq_lens, "seq_lens", q.shape[0], q)
     Bs, Hq, D = q.shape
