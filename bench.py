@@ -27,8 +27,8 @@ each valid cached K/V byte once plus q and O.
 
 Outside the step (not in `value`), the bench also times the two short forwards,
 B4 H16 N2048 D128 bf16 non-causal and causal, and the fp32 forward B1 H2 N256 D64.
-That last kernel is shorter than the binding's host cost per call, so its line gives
-the eager time as `eager_ms` and, as `ms`, the GPU time per call of 200 calls
+That last kernel takes about as long as the binding's host cost per call, so its line
+gives the eager time as `eager_ms` and, as `ms`, the GPU time per call of 200 calls
 captured into one HIP graph.
 
 Prints one JSON line.  The CPU baseline times the fp64 oracle on bounded samples of
@@ -768,8 +768,9 @@ def main():
             leg = FwdLeg(cfg)
             out_legs[name] = flops_rec(leg, time_aux(leg, stream, reps=20 if cfg["N"] > 1024 else 200))
             if cfg["N"] <= 1024:
-                # the binding's host cost per call (about 20 us) exceeds this kernel: the eager
-                # figure above is host-bound, so report the GPU time of a graph of the calls too
+                # the binding's host cost per call (about 15 us) is as long as this kernel, so
+                # the eager figure above is bound by the host: report the GPU time per call of
+                # a graph of the calls as `ms`, and the eager figure beside it
                 out_legs[name]["eager_ms"] = out_legs[name]["ms"]
                 gr = flops_rec(leg, time_graph(leg))
                 out_legs[name].update(ms=gr["ms"], tflops=gr["tflops"], frac_bf16_peak=gr["frac_bf16_peak"],
