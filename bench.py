@@ -532,11 +532,44 @@ def mfma_ceiling(pattern: int, seconds: float = 1.0) -> float:
     return 4 * lib.fa_ceiling_mfma_flops(wgs, iters) / t / 1e12
 
 
+def stream_ceiling(gib: int = 4, wgs_per_cu: int = 4) -> float:
+    """GB/s of libfa_ceiling's plain streaming read of `gib` GiB (each byte read once,
+    16-byte non-temporal loads, eight in flight per thread): the HBM read rate a kernel
+    that reads its bytes once, as the decode does, can reach."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "io_aware_tiled_10_amd", "libfa_ceiling.so"))
+    lib.fa_ceiling_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    wgs = wgs_per_cu * torch.cuda.get_device_properties(DEV).multi_processor_count
+    nbytes = ((gib << 30) // (32768 * wgs)) * 32768 * wgs
+    src = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    out = torch.empty(wgs * 256, dtype=torch.int32, device=DEV)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        if lib.fa_ceiling_stream(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()), wgs,
+                                 ctypes.c_void_p(stream)):
+            raise RuntimeError("fa_ceiling_stream failed")
+
+    for _ in range(2):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    del src, out
+    return nbytes / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9
+
+
 def ceilings():
     """Achievable rates on this GPU for the same data statistics, for context: the
     matrix cores alone on register-resident operands (random-like and all-ones), a
     library bf16 GEMM (hipBLASLt via torch.matmul, 8192^3) on N(0,1) data and on all-ones
-    data (the sustained clock depends on the data), and a 2 GiB device-to-device copy."""
+    data (the sustained clock depends on the data), a 2 GiB device-to-device copy, and a
+    plain streaming read of 4 GiB."""
     res = {}
     res["mfma_loop_bf16_random_tflops"] = round(mfma_ceiling(0), 1)
     res["mfma_loop_bf16_ones_tflops"] = round(mfma_ceiling(1), 1)
@@ -572,6 +605,7 @@ def ceilings():
     torch.cuda.synchronize()
     res["device_copy_2gib_read_plus_write_gbs"] = round(2 * x.numel() * 2 / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9, 1)
     del x, y
+    res["stream_read_4gib_gbs"] = round(stream_ceiling(), 1)
     return res
 
 

@@ -1,5 +1,6 @@
-// fa_ceiling.hip -- measurement aid: the sustained rate of the bf16 matrix cores on this
-// part with operands of a given bit pattern and no memory traffic at all.
+// fa_ceiling.hip -- measurement aids: the sustained rate of the bf16 matrix cores on this
+// part with operands of a given bit pattern and no memory traffic at all, and the HBM read
+// rate of a plain streaming kernel.
 //
 // The attention kernels are priced against the published dense bf16 peak.  How much of
 // that peak the chip sustains depends on the data the matrix cores multiply (their power
@@ -65,8 +66,42 @@ mfma_ceiling_kernel(float* out, int iters, int pattern) {
   out[tid] = s;  // keeps every product live
 }
 
+constexpr int kStreamThreads = 256, kStreamInFlight = 8;
+
+// HBM streaming read: workgroup g reads its contiguous slice of `per` 16-byte elements with
+// non-temporal loads, kStreamInFlight of them in flight per thread, and stores one word per
+// thread (the XOR of what it read, so that no load is dropped).
+__global__ void __launch_bounds__(kStreamThreads) stream_read_kernel(const u32x4_t* src, int64_t per,
+                                                                     uint32_t* out) {
+  const u32x4_t* p = src + (int64_t)blockIdx.x * per;
+  uint32_t acc = 0;
+  for (int64_t i = threadIdx.x; i < per; i += kStreamThreads * kStreamInFlight) {
+    u32x4_t v[kStreamInFlight];
+#pragma unroll
+    for (int u = 0; u < kStreamInFlight; ++u) v[u] = __builtin_nontemporal_load(p + i + kStreamThreads * u);
+#pragma unroll
+    for (int u = 0; u < kStreamInFlight; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  out[blockIdx.x * kStreamThreads + threadIdx.x] = acc;
+}
+
 }  // namespace
 }  // namespace fa
+
+extern "C" int fa_ceiling_stream(const void* src, int64_t bytes, unsigned int* out, int workgroups,
+                                 void* stream) {
+  const int64_t chunk = (int64_t)16 * fa::kStreamThreads * fa::kStreamInFlight;  // one trip of a workgroup
+  if (!src || !out || workgroups < 1 || bytes <= 0 || bytes % (chunk * workgroups) != 0) return 1;
+  if (reinterpret_cast<uintptr_t>(src) & 15u) return 1;
+  const fa::u32x4_t* s = static_cast<const fa::u32x4_t*>(src);
+  int64_t per = bytes / 16 / workgroups;
+  uint32_t* o = out;
+  void* args[] = {&s, &per, &o};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fa::stream_read_kernel),
+                                       dim3((unsigned)workgroups), dim3(fa::kStreamThreads), args, 0,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? 0 : 2;
+}
 
 extern "C" int fa_ceiling_mfma(float* out, int workgroups, int iters, int pattern, void* stream) {
   if (!out || workgroups < 1 || iters < 1 || (pattern != 0 && pattern != 1)) return 1;

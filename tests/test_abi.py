@@ -48,7 +48,7 @@ def test_ceiling_library_exports_its_header_and_rejects_bad_arguments():
     path = os.path.join(ROOT, "io_aware_tiled_10_amd", "libfa_ceiling.so")
     text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
     declared = set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text))
-    assert declared == {"fa_ceiling_mfma", "fa_ceiling_mfma_flops"}
+    assert declared == {"fa_ceiling_mfma", "fa_ceiling_mfma_flops", "fa_ceiling_stream"}
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
     assert declared <= set(re.findall(r"\sT\s(fa_\w+)", out))
     h = ctypes.CDLL(path)
@@ -62,6 +62,15 @@ def test_ceiling_library_exports_its_header_and_rejects_bad_arguments():
     assert h.fa_ceiling_mfma(FAKE, 1, 1, 2, None) == 1
     # 8 waves x 16 products of 32 x 32 x 16 per trip
     assert h.fa_ceiling_mfma_flops(3, 5) == 3 * 8 * 5 * 16 * 2 * 32 * 32 * 16
+    h.fa_ceiling_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    ok_bytes = 32768 * 4
+    assert h.fa_ceiling_stream(None, ok_bytes, FAKE, 4, None) == 1
+    assert h.fa_ceiling_stream(FAKE, ok_bytes, None, 4, None) == 1
+    assert h.fa_ceiling_stream(FAKE, ok_bytes, FAKE, 0, None) == 1
+    assert h.fa_ceiling_stream(FAKE, 0, FAKE, 4, None) == 1
+    assert h.fa_ceiling_stream(FAKE, ok_bytes + 16, FAKE, 4, None) == 1  # not whole trips
+    assert h.fa_ceiling_stream(FAKE, ok_bytes, FAKE, 3, None) == 1      # slices of unequal trips
+    assert h.fa_ceiling_stream(FAKE + 8, ok_bytes, FAKE, 4, None) == 1  # misaligned
 
 
 def test_status_strings_and_version():
