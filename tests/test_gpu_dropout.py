@@ -44,6 +44,9 @@ CASES = [
     ("mha_ragged_causal", 1, 2, 2, 300, 300, 128, True, None),
     ("gqa_noncausal", 2, 4, 2, 200, 257, 128, False, None),
     ("kvlens_d64", 2, 2, 1, 150, 260, 64, True, [17, 259]),
+    # mid sizes: the kernels' block loops run for many trips
+    ("gqa4_n1100_causal", 1, 8, 2, 1100, 1100, 128, True, None),
+    ("mha_d64_nq900_nk1300_kvlens", 2, 2, 2, 900, 1300, 64, True, [1300, 611]),
 ]
 
 
