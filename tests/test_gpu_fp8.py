@@ -38,6 +38,9 @@ CASES = [
     ("gqa_ragged_causal", 1, 8, 2, 257, 257, True, None),
     ("causal_nq_lt_nk", 1, 2, 1, 100, 333, True, None),
     ("kvlens", 2, 2, 1, 130, 300, False, [300, 61]),
+    # mid sizes: the block loop runs for many trips, across many 64-row scale blocks
+    ("gqa4_n1100_causal", 1, 8, 2, 1100, 1100, True, None),
+    ("mha_nq700_nk1500_kvlens_causal", 2, 2, 2, 700, 1500, True, [1500, 333]),
 ]
 
 
