@@ -32,6 +32,8 @@ VARLEN = [
     # groups of 4 query heads per KV head, causal: tiles of 64 rows x 4 heads
     ("gqa4_causal_ragged", [700, 65, 300], [700, 65, 300], 8, 2, 128, True),
     ("gqa4_causal_nq_ne_nk_d64", [150, 400], [300, 390], 8, 2, 64, True),
+    # mid sizes: long block loops beside short sequences in one packed batch
+    ("gqa4_causal_mid_sizes", [1500, 2049, 33, 900], [1500, 2049, 33, 900], 8, 2, 128, True),
 ]
 
 
