@@ -609,6 +609,33 @@ def ceilings():
     return res
 
 
+def _gpu_clock_info():
+    """The graphics clock range and power cap the GPU reports (amd-smi, rocm-smi; read
+    once, in child processes), or None where a tool is missing.  The clock is not locked
+    on these parts: it floats under the power cap, which is why rates move from box to box."""
+    import subprocess
+    info = {}
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout)
+        gpus = data["gpu_data"] if isinstance(data, dict) else data
+        clk = gpus[0]["clock"]
+        gfx = [v for k, v in clk.items() if k.startswith("gfx")]
+        info["gfx_clk_max_mhz"] = gfx[0]["max_clk"]["value"]
+        info["gfx_clk_min_mhz"] = gfx[0]["min_clk"]["value"]
+        info["gfx_clk_locked"] = gfx[0].get("clk_locked")
+    except Exception:  # pragma: no cover - tool missing or output changed
+        pass
+    try:
+        r = subprocess.run(["rocm-smi", "--showmaxpower", "--json"], capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout[r.stdout.index("{"):])
+        card = next(iter(data.values()))
+        info["power_cap_w"] = float(next(v for k, v in card.items() if "Power" in k))
+    except Exception:  # pragma: no cover
+        pass
+    return info or None
+
+
 def _code_only(text: str) -> str:
     """The source with comments and blank lines removed, so that a change to comments
     alone does not retire a counter summary taken on the same machine code."""
@@ -901,7 +928,8 @@ def main():
         line["ceilings"] = ceil
     props = torch.cuda.get_device_properties(0)
     line["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
-                      "hip_runtime": getattr(torch.version, "hip", None), "cus": props.multi_processor_count}
+                      "hip_runtime": getattr(torch.version, "hip", None), "cus": props.multi_processor_count,
+                      "clocks": _gpu_clock_info()}
     print(json.dumps(line), flush=True)
     if parity is not None and not parity["pass"]:
         log("parity check FAILED: " + json.dumps(parity))
