@@ -60,11 +60,14 @@ def test_fwd_writes_nothing_outside_o_and_lse(out_dtype):
         assert bits_equal(go.t, ref[0]) and bits_equal(gl.t, ref[1])
 
 
-def test_fwd_f32_writes_nothing_outside_o_and_lse():
-    say("guards fwd fp32")
-    x = inputs.attention_inputs(1, 2, 2, 257, 257, 64, "fp32", seed=42)
+# (B, H, N): 16-row tiles (few tiles) and 64-row tiles (512 or more of them)
+@pytest.mark.parametrize("shape", [(1, 2, 257), (1, 64, 513)], ids=["small_grid", "wide_grid"])
+def test_fwd_f32_writes_nothing_outside_o_and_lse(shape):
+    B, H, N = shape
+    say(f"guards fwd fp32 {shape}")
+    x = inputs.attention_inputs(B, H, H, N, N, 64, "fp32", seed=42)
     q, k, v = (to_dev(a, torch.float32) for a in (x.q, x.k, x.v))
-    go, gl = Guarded((1, 2, 257, 64), torch.float32, gap=16), Guarded((1, 2, 257), torch.float32)
+    go, gl = Guarded((B, H, N, 64), torch.float32, gap=16), Guarded((B, H, N), torch.float32)
     fa.fwd(q, k, v, causal=True, out=go.t, lse_out=gl.t)
     ref = fa.fwd(q, k, v, causal=True)
     assert go.intact() and gl.intact()
