@@ -55,6 +55,27 @@ def test_fwd_nan_reaches_exactly_the_rows_that_see_it(causal, out_dtype):
     say(f"  {n} NaN rows, as planted")
 
 
+# fp32 inputs: (H, N) with 16-row tiles (few tiles) and with 64-row tiles (512 or more)
+@pytest.mark.parametrize("shape", [(2, 300), (64, 520)], ids=["small_grid", "wide_grid"])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+def test_fwd_fp32_nan_reaches_exactly_the_rows_that_see_it(shape, causal):
+    H, N = shape
+    say(f"fwd fp32 NaN {shape} causal={causal}")
+    x = inputs.attention_inputs(1, H, H, N, N, 64, "fp32", seed=23)
+    q, k = x.q.copy(), x.k.copy()
+    q[0, 1, 5, 3] = np.nan          # query row 5 of head 1
+    k[0, 0, 170, 2] = np.nan        # key 170 of head 0
+    o, lse = fa.fwd(to_dev(q, torch.float32), to_dev(k, torch.float32), to_dev(x.v, torch.float32),
+                    causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(q, k, x.v, None, causal)
+    expect = np.zeros((1, H, N), bool)
+    expect[0, 1, 5] = True
+    expect[0, 0, 170 if causal else 0:] = True
+    n = check_rows(to_host(o), to_host(lse), o_ref, lse_ref, False, expect)
+    say(f"  {n} NaN rows, as planted")
+
+
 def test_decode_nan_reaches_exactly_the_heads_that_see_it():
     say("decode NaN")
     rng = np.random.default_rng(22)
